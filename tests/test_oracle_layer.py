@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle of the int8 linear layer (CPU only).
+
+Each check ties the oracle to something other than itself:
+* brute force over exact rationals on tiny inputs (quantizer, forward,
+  backward, grad_bias), written with Python loops;
+* closed-form special cases that reduce to textbook integer or float matmuls;
+* invariants of the quantizer on the workloads' own data;
+* an implementation-free error bound against the unquantized product;
+* the error bounds of bitsandbytes PR #33's module test at small shapes.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle.formats import to_f64, to_half
+from tests._exact import exact_round, fl32, round_half_even
+
+# --------------------------------------------------------------------------
+# brute force (exact rationals)
+
+F127 = Fraction(127)
+INV127 = fl32(Fraction(1, 127))
+
+
+def bf_quantize(X16_vals, tau):
+    """Exact-rational quantizer; X16_vals: R x C list of fp16 values as Fractions."""
+    R = len(X16_vals)
+    C = len(X16_vals[0]) if R else 0
+    on = tau is not None and 0 < tau < float("inf")
+    t = Fraction(float(np.float32(tau))) if on else None
+    O = [c for c in range(C) if on and any(abs(X16_vals[r][c]) > t for r in range(R))]
+    codes, codes_exact_real, scales = [], [], []
+    for r in range(R):
+        s = Fraction(0)
+        for c in range(C):
+            if c not in O:
+                s = max(s, abs(X16_vals[r][c]))
+        inv = fl32(F127 / s) if s > 0 else Fraction(0)
+        row, row_real = [], []
+        for c in range(C):
+            if c in O or s == 0:
+                row.append(0)
+                row_real.append(0)
+                continue
+            v = fl32(X16_vals[r][c] * inv)                 # fp32 product, exactly rounded
+            row.append(max(-127, min(127, round_half_even(v))))
+            row_real.append(max(-127, min(127, round_half_even(F127 * X16_vals[r][c] / s))))
+        codes.append(row)
+        codes_exact_real.append(row_real)
+        scales.append(s)
+    sub = [[X16_vals[r][c] for c in O] for r in range(R)]
+    return codes, codes_exact_real, scales, O, sub
+
+
+def _tiny_fp16(g, R, C):
+    kind = g.integers(0, 4)
+    if kind == 0:
+        x = g.standard_normal((R, C)) * 3
+    elif kind == 1:
+        x = g.integers(-8, 9, (R, C)).astype(np.float64)            # ties, repeats, zeros
+    elif kind == 2:
+        x = g.standard_normal((R, C)) * np.ldexp(1.0, g.integers(-20, 4))
+    else:
+        x = g.standard_normal((R, C))
+        x[:, g.integers(0, C)] *= 20
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32", "bf16"])
+def test_quantizer_brute_force(dt):
+    g = np.random.default_rng(100 + ["f16", "f32", "bf16"].index(dt))
+    near_half = 0
+    total = 0
+    for case in range(700):
+        R, C = int(g.integers(1, 7)), int(g.integers(1, 7))
+        x16 = _tiny_fp16(g, R, C)
+        if dt == "f16":
+            X = x16
+        elif dt == "f32":
+            X = (x16.astype(np.float32) + g.standard_normal((R, C)).astype(np.float32) * 1e-4)
+        else:
+            X = workloads._store(x16.astype(np.float32), "bf16")
+        tau = float(g.choice([6.0, 2.0, 0.0, np.inf, 1.5, 4.0]))
+        X16 = to_half(X, dt)
+        vals = [[Fraction(float(v)) for v in row] for row in X16]
+        codes, real, scales, O, sub = bf_quantize(vals, tau)
+        q = oracle.quantize_rowwise(X, dt, tau)
+        assert q["outliers"].tolist() == O
+        assert [Fraction(float(s)) for s in q["scale"]] == scales
+        assert q["codes"].tolist() == codes
+        assert [[Fraction(float(v)) for v in row] for row in q["sub"]] == sub
+        total += R * C
+        near_half += sum(a != b for ra, rb in zip(codes, real) for a, b in zip(ra, rb))
+    # The fp32 formula equals exact rounding of 127*x/s except within ~2^-22
+    # of a half-integer; such cases must be rare on these inputs.
+    assert near_half <= total * 0.002
+
+
+def test_threshold_is_strict_and_off_values():
+    X = np.array([[6.0, 1.0, -6.0], [0.5, 6.0078125, 2.0]], dtype=np.float16)
+    q = oracle.quantize_rowwise(X, "f16", 6.0)
+    assert q["outliers"].tolist() == [1]                      # 6.0 is not > 6.0
+    for off in (0.0, -1.0, float("inf"), float("nan")):
+        assert oracle.quantize_rowwise(X, "f16", off)["outliers"].size == 0
+
+
+def test_zero_rows_and_all_outlier_rows():
+    X = np.array([[0, 0, 0], [7, 0, 0], [7, 1, -2]], dtype=np.float16)
+    q = oracle.quantize_rowwise(X, "f16", 6.0)
+    assert q["outliers"].tolist() == [0]
+    assert q["scale"].tolist() == [0.0, 0.0, 2.0]
+    assert q["codes"].tolist() == [[0, 0, 0], [0, 0, 0], [0, 64, -127]]
+    assert q["sub"].astype(np.float64).ravel().tolist() == [0.0, 7.0, 7.0]
+
+
+# --------------------------------------------------------------------------
+# invariants on the workloads' data
+
+
+def _wl_rows(name, li, rows):
+    wl = workloads.WORKLOADS[name]
+    return workloads.make_activation(wl, li, rows=rows), wl
+
+
+@pytest.mark.parametrize("name,li", [("single4096", 0), ("llama7b_mlp", 2), ("llama7b_block", 4),
+                                     ("mlp600", 0)])
+def test_quantizer_invariants(name, li):
+    A, wl = _wl_rows(name, li, 256 if name != "mlp600" else None)
+    dt, tau = wl.dtype, wl.threshold
+    q = oracle.quantize_rowwise(A, dt, tau)
+    X = to_half(A, dt).astype(np.float64)
+    codes, s, O = q["codes"].astype(np.int64), q["scale"].astype(np.float64), q["outliers"]
+    keep = np.ones(X.shape[1], bool)
+    keep[O] = False
+    # (i) range, never -128
+    assert codes.min() >= -127 and codes.max() <= 127
+    # (ii) absmax element maps to +-127
+    for r in range(X.shape[0]):
+        if s[r] > 0:
+            c = np.argmax(np.where(keep, np.abs(X[r]), -1))
+            assert abs(codes[r, c]) == 127
+    # (iii) sign
+    assert np.all((np.sign(codes) == np.sign(X)) | (codes == 0))
+    # (iv) monotone within a row
+    for r in range(0, X.shape[0], 17):
+        o = np.argsort(X[r, keep], kind="stable")
+        assert np.all(np.diff(codes[r, keep][o]) >= 0)
+    # (v) outlier columns leave the int8 path and are copied bit for bit
+    assert np.all(codes[:, O] == 0)
+    assert np.array_equal(q["sub"].view(np.uint16), to_half(A, dt)[:, O].view(np.uint16))
+    # (vi) remaining magnitudes are within tau
+    assert np.all(s <= tau)
+    # (vii) tau off => no outliers
+    assert oracle.quantize_rowwise(A, dt, float("inf"))["outliers"].size == 0
+    # seeded outlier columns are detected
+    seeded = workloads.outlier_columns(wl.wid, li, wl.layers[li].K, wl.layers[li].n_outliers)
+    assert set(seeded.tolist()) <= set(O.tolist())
+
+
+def test_quantizer_scale_equivariance():
+    A, wl = _wl_rows("single4096", 0, 64)
+    q0 = oracle.quantize_rowwise(A, "f16", 0.0)
+    for e in (-3, 2):
+        A2 = (A.astype(np.float64) * 2.0 ** e).astype(np.float16)
+        q1 = oracle.quantize_rowwise(A2, "f16", 0.0)
+        assert np.array_equal(q1["codes"], q0["codes"])
+        assert np.array_equal(q1["scale"].astype(np.float64), q0["scale"].astype(np.float64) * 2.0 ** e)
+
+
+# --------------------------------------------------------------------------
+# closed-form special cases
+
+
+def _int_weights(g, N, K):
+    """Integer weights in [-127, 127] with +-127 in every row: quantize to themselves."""
+    W = g.integers(-127, 128, (N, K)).astype(np.float32)
+    W[np.arange(N), g.integers(0, K, N)] = np.where(g.random(N) < 0.5, -127, 127)
+    return W
+
+
+def test_integer_forward_is_textbook_matmul():
+    g = np.random.default_rng(20)
+    M, K, N = 37, 70, 29
+    A = _int_weights(g, M, K)          # same construction: every row has |127|
+    W = _int_weights(g, N, K)
+    CB, SCB = oracle.quantize_weight(W)
+    assert np.array_equal(CB, W.astype(np.int8)) and np.all(SCB == 127)
+    f = oracle.linear_forward(A, "f32", CB, SCB, None, float("inf"))
+    assert np.array_equal(f["q"]["codes"], A.astype(np.int8))
+    ref = A.astype(np.int64) @ W.astype(np.int64).T
+    assert np.array_equal(f["c32"], ref)
+    # y = C32 * 127 * 127 / 127^2 = C32 exactly
+    assert np.array_equal(f["y"], ref.astype(np.float64))
+
+
+def test_zero_input_gives_bias_bitwise():
+    g = np.random.default_rng(21)
+    for dt in ("f16", "bf16", "f32"):
+        W = g.standard_normal((13, 40)).astype(np.float32) * 0.02
+        CB, SCB = oracle.quantize_weight(W)
+        b = workloads._store(g.standard_normal(13).astype(np.float32) * 0.01, dt)
+        A = workloads._store(np.zeros((5, 40), np.float32), dt)
+        f = oracle.linear_forward(A, dt, CB, SCB, b, 6.0)
+        assert np.array_equal(np.asarray(f["out"]).view(np.uint8),
+                              np.broadcast_to(b, (5, 13)).view(np.uint8))
+
+
+def test_threshold_off_equals_dequantized_int8_product():
+    g = np.random.default_rng(22)
+    M, K, N = 50, 96, 40
+    A = (g.standard_normal((M, K)) * 2).astype(np.float16)
+    W = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    CB, SCB = oracle.quantize_weight(W)
+    f = oracle.linear_forward(A, "f16", CB, SCB, None, float("inf"))
+    q = f["q"]
+    deqA = q["codes"].astype(np.float64) * (q["scale"].astype(np.float64)[:, None] / 127)
+    deqW = CB.astype(np.float64) * (SCB.astype(np.float64)[:, None] / 127)
+    assert np.allclose(f["y"], deqA @ deqW.T, rtol=1e-12, atol=1e-12)
+
+
+def test_all_outlier_columns_is_textbook_float_matmul():
+    g = np.random.default_rng(23)
+    M, K, N = 40, 33, 21
+    A = (g.uniform(0.5, 2, (M, K)) * np.where(g.random((M, K)) < .5, -1, 1)).astype(np.float16)
+    W = _int_weights(g, N, K)                     # SCB = 127 -> Wdq = CB exactly
+    CB, SCB = oracle.quantize_weight(W)
+    b = (g.standard_normal(N) * 0.01).astype(np.float16)
+    f = oracle.linear_forward(A, "f16", CB, SCB, b, 1e-3)
+    q = f["q"]
+    assert q["outliers"].tolist() == list(range(K))
+    assert np.all(q["codes"] == 0) and np.all(q["scale"] == 0)
+    ref = A.astype(np.float64) @ W.astype(np.float64).T + b.astype(np.float64)
+    assert np.allclose(f["y"], ref, rtol=1e-13, atol=1e-12)
+
+
+def test_integer_backward_is_textbook_matmul():
+    g = np.random.default_rng(24)
+    M, N, K = 45, 31, 66
+    W = _int_weights(g, N, K)
+    CB, SCB = oracle.quantize_weight(W)
+    sig = (SCB * np.float32(1) / np.float32(127))
+    assert np.all(oracle.dequant_weight(CB, SCB) == CB.astype(np.float16))
+    G = g.integers(-1, 2, (M, N)).astype(np.float32)
+    b = oracle.linear_backward_input(G, "f32", CB, SCB)
+    ref = G.astype(np.int64) @ W.astype(np.int64)
+    assert np.array_equal(b["grad_A"], ref.astype(np.float32))
+    del sig
+
+
+def test_dequant_constant_is_one_for_scale_127():
+    assert np.float32(127) * (np.float32(1) / np.float32(127)) == np.float32(1.0)
+
+
+# --------------------------------------------------------------------------
+# brute force of the whole forward / backward on tiny inputs
+
+
+def _tiny_layer(g, M, K, N, dt):
+    x = (g.standard_normal((M, K)) * 2).astype(np.float32)
+    x[:, g.integers(0, K)] *= 8
+    A = workloads._store(x, dt)
+    W = (g.standard_normal((N, K)) * 0.05).astype(np.float32)
+    b = workloads._store((g.standard_normal(N) * 0.1).astype(np.float32), dt)
+    G = workloads._store((g.standard_normal((M, N)) * 0.5).astype(np.float32), dt)
+    return A, W, b, G
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_forward_backward_brute_force(dt):
+    g = np.random.default_rng(30 + ["f16", "bf16", "f32"].index(dt))
+    for case in range(25):
+        M, K, N = int(g.integers(1, 6)), int(g.integers(1, 7)), int(g.integers(1, 6))
+        A, W, b, G = _tiny_layer(g, M, K, N, dt)
+        tau = 6.0
+        CB, SCB = oracle.quantize_weight(W)
+        f = oracle.linear_forward(A, dt, CB, SCB, b, tau)
+        X16 = [[Fraction(float(v)) for v in row] for row in to_half(A, dt)]
+        codes, _, s, O, sub = bf_quantize(X16, tau)
+        bvals = [Fraction(float(v)) for v in to_f64(b, dt)]
+        # weights: exact quantization of W (tau off) by the same brute force
+        W16 = [[Fraction(float(v)) for v in row] for row in W.astype(np.float16)]
+        # (weights quantize from fp32 -> fp16 cast first, as activations do)
+        cbs, _, sbs, _, _ = bf_quantize(W16, None)
+        assert CB.tolist() == cbs and [Fraction(float(v)) for v in SCB] == sbs
+        sig = [fl32(sb * INV127) for sb in sbs]
+        wdq = [[exact_round(fl32(Fraction(cbs[n][k]) * sig[n]), "f16") for k in range(K)]
+               for n in range(N)]
+        for m in range(M):
+            for n in range(N):
+                acc = sum(Fraction(codes[m][k] * cbs[n][k]) for k in range(K))
+                assert f["c32"][m, n] == acc
+                terms = [acc * s[m] * sbs[n] / 16129]
+                terms += [sub[m][j] * wdq[n][O[j]] for j in range(len(O))]
+                terms += [bvals[n]]
+                y = sum(terms)
+                mag = sum(abs(t) for t in terms)
+                # float64 evaluation: a few roundings, each within 2^-53 of the magnitudes
+                assert abs(Fraction(float(f["y"][m, n])) - y) <= mag * Fraction(1, 2 ** 48) + Fraction(1, 2 ** 200)
+        bw = oracle.linear_backward_input(G, dt, CB, SCB)
+        G16 = [[Fraction(float(v)) for v in row] for row in to_half(G, dt)]
+        for m in range(M):
+            for k in range(K):
+                terms = [G16[m][n] * wdq[n][k] for n in range(N)]
+                y = sum(terms)
+                mag = sum(abs(t) for t in terms)
+                assert abs(Fraction(float(bw["y"][m, k])) - y) <= mag * Fraction(1, 2 ** 48) + Fraction(1, 2 ** 200)
+        gb64, gbD = oracle.grad_bias(G, dt)
+        Gv = to_f64(G, dt)
+        for n in range(N):
+            exact = sum(Fraction(float(Gv[m, n])) for m in range(M))
+            mag = sum(abs(Fraction(float(Gv[m, n]))) for m in range(M))
+            assert abs(Fraction(float(gb64[n])) - exact) <= mag * Fraction(1, 2 ** 48)
+
+
+def test_rows_subset_matches_full():
+    g = np.random.default_rng(40)
+    A, W, b, G = _tiny_layer(g, 70, 40, 30, "bf16")
+    CB, SCB = oracle.quantize_weight(W)
+    full = oracle.linear_forward(A, "bf16", CB, SCB, b, 6.0)
+    rows = np.array([3, 0, 69, 12])
+    part = oracle.linear_forward(A, "bf16", CB, SCB, b, 6.0, rows=rows)
+    assert np.array_equal(part["out"], full["out"][rows])
+    bf = oracle.linear_backward_input(G, "bf16", CB, SCB)
+    bp = oracle.linear_backward_input(G, "bf16", CB, SCB, rows=rows)
+    assert np.array_equal(bp["grad_A"], bf["grad_A"][rows])
+
+
+# --------------------------------------------------------------------------
+# error bounds against the unquantized product
+
+
+def test_closed_form_error_bound_against_true_product():
+    """|y - A16 W^T| <= sum_k |a| e_w + |w| e_a + e_a e_w (+ outlier-product rounding),
+    e_a = (1/2 + 2^-20) SCA/127, e_w = (1/2 + 2^-20) SCB/127 (tau off)."""
+    g = np.random.default_rng(41)
+    M, K, N = 64, 256, 48
+    A = g.standard_normal((M, K)).astype(np.float16)
+    W = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    CB, SCB = oracle.quantize_weight(W)
+    f = oracle.linear_forward(A, "f16", CB, SCB, None, float("inf"))
+    a = A.astype(np.float64)
+    w = W.astype(np.float16).astype(np.float64)
+    ea = (0.5 + 2 ** -20) * f["q"]["scale"].astype(np.float64) / 127
+    ew = (0.5 + 2 ** -20) * SCB.astype(np.float64) / 127
+    bound = (np.abs(a).sum(1)[:, None] * ew[None, :] + ea[:, None] * np.abs(w).sum(1)[None, :]
+             + K * ea[:, None] * ew[None, :])
+    err = np.abs(f["y"] - a @ w.T)
+    assert np.all(err <= bound * (1 + 1e-9))
+    # and the bound is not vacuous
+    assert err.max() > 0.05 * bound.max()
+
+
+def test_page_bounds_two_stacked_layers_small_shape():
+    """bitsandbytes PR #33 module-test design: the input gradient through two
+    int8 layers (32 -> 64 -> 32, 128 tokens) against grad_proj @ W2 @ W1 with
+    fp16 weights; max err <= 0.05*mean|ref| and <= 0.5 % of elements outside
+    (atol 0.01*mean|ref|, rtol 0.1). Weights use torch.nn.Linear's default
+    init U(-1/sqrt(fan_in), 1/sqrt(fan_in)) (reading: the page does not state it)."""
+    g = np.random.default_rng(42)
+    M, K, H, N = 128, 32, 64, 32
+    for rep in range(6):
+        W1 = g.uniform(-1 / np.sqrt(K), 1 / np.sqrt(K), (H, K)).astype(np.float32)
+        W2 = g.uniform(-1 / np.sqrt(H), 1 / np.sqrt(H), (N, H)).astype(np.float32)
+        gp = g.standard_normal((M, N)).astype(np.float16)
+        cb1, s1 = oracle.quantize_weight(W1)
+        cb2, s2 = oracle.quantize_weight(W2)
+        g1 = oracle.linear_backward_input(gp, "f16", cb2, s2)["grad_A"]
+        gx = oracle.linear_backward_input(g1, "f16", cb1, s1)["grad_A"]
+        w1h = W1.astype(np.float16).astype(np.float64)
+        w2h = W2.astype(np.float16).astype(np.float64)
+        r = oracle.page_bounds(gx, gp.astype(np.float64) @ w2h @ w1h)
+        assert r["ok"], r
+    # a plausible slip (dequantizing with the wrong row's scale) breaks the bound
+    bad = oracle.linear_backward_input(g1, "f16", cb1, np.roll(s1, 1))["grad_A"]
+    assert not oracle.page_bounds(bad, g1.astype(np.float64) @ w1h)["ok"]
+
+
+def test_page_bounds_detect_a_planted_error():
+    ref = np.random.default_rng(43).standard_normal(10000)
+    T = ref.copy()
+    assert oracle.page_bounds(T, ref)["ok"]
+    T[:100] += 0.5 * np.abs(ref).mean()        # 1% of elements off by half the scale
+    assert not oracle.page_bounds(T, ref)["ok"]
+
+
+# --------------------------------------------------------------------------
+# the residual MLP of the EasyDeL example
+
+
+def _mlp600_weights():
+    wl = workloads.WORKLOADS["mlp600"]
+    Ws = [workloads.make_weight(wl, i) for i in range(2)]
+    bs = [workloads.make_bias(wl, i) for i in range(2)]
+    return wl, Ws, bs
+
+
+def test_silu_grad_finite_difference():
+    h = np.linspace(-8, 8, 1001)
+    fd = (oracle.silu(h + 1e-6) - oracle.silu(h - 1e-6)) / 2e-6
+    assert np.allclose(oracle.silu_grad(h), fd, atol=1e-8)
+
+
+def test_mlp600_magnitude_against_printed_example():
+    """Parity unpinned (JAX streams / fjformer quantizer): magnitude check only.
+
+    The printed int8-vs-float gap of the example is below 0.05*mean|out|; the
+    oracle's int8 MLP must be in the same class against its float twin."""
+    rows = np.loadtxt(__file__.replace("test_oracle_layer.py", "golden/easydel66_mlp_printed.txt"))
+    fp, i8 = rows[:, 1:5], rows[:, 5:9]
+    printed = oracle.page_bounds(i8, fp)
+    assert printed["ok"]
+    wl, Ws, bs = _mlp600_weights()
+    x = workloads.make_activation(wl, 0)
+    g = workloads.make_grad(wl, 1)
+    layers = []
+    for W, b in zip(Ws, bs):
+        cb, s = oracle.quantize_weight(W)
+        layers.append((cb, s, b))
+    r = oracle.mlp_forward_backward(x, g, "f32", layers, wl.threshold)
+    xf = x.astype(np.float64)
+    h = xf @ Ws[0].astype(np.float64).T
+    ref = oracle.silu(h) @ Ws[1].astype(np.float64).T + xf
+    mine = oracle.page_bounds(r["out"], ref)
+    assert mine["ok"], mine
+    assert mine["max_rel"] < 5 * printed["max_rel"] + 0.02

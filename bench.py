@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the int8 linear layer's hot path on one MI355X.
+
+One step = the whole path over one batch for every linear of the workload:
+for each layer, the forward call (fp16 cast, outlier columns, row-wise int8
+quantization, int8 MFMA GEMM with fused dequant / outlier product / bias /
+cast) and the memory-efficient backward call (fp16 MFMA GEMM over int8
+weights dequantized on the fly, plus grad_bias when the layer has a bias).
+Weights are quantized once before timing (offline step of the layer).
+
+Default workload: the 7B decoder-block linear set (q, k, v, o 4096x4096;
+gate/up 4096->11008; down 11008->4096; 4096 tokens, bf16, 0.1 % outlier
+columns x20, threshold 6.0). Inputs are synthetic and resident in HBM;
+several input sets rotate so the footprint exceeds the 256 MB Infinity Cache.
+
+Prints ONE JSON line. value = effective TOPS = sum over layers of 4*M*N*K
+(2MNK int8 ops forward + 2MNK fp16 flops backward) / time per step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "int8 linear fwd+bwd effective TOPS at 7B shapes; % of int8 MFMA peak"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA, TFLOP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+
+TORCH_DT = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_gpu_inputs(wl, n_sets, seed_base=1234):
+    """Per layer: weights (quantized by the library) and n_sets (A, G) pairs drawn on the GPU
+    with the workload's recipe (N(0,1) activations, seeded outlier columns scaled, grad ~ N(0, std))."""
+    import torch
+
+    import int8_quantized_linear_rowwise_amd as I8
+    import workloads
+
+    dt = getattr(torch, TORCH_DT[wl.dtype])
+    dev = "cuda:0"
+    layers = []
+    for li, L in enumerate(wl.layers):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed_base + 101 * li)
+        W = torch.randn((L.N, L.K), generator=gen, device=dev, dtype=torch.float32) * wl.w_std
+        CB, SCB = I8.quantize_weight(W)
+        del W
+        bias = None
+        if L.has_bias:
+            bias = (torch.randn((L.N,), generator=gen, device=dev) * wl.bias_std).to(dt)
+        cols = torch.from_numpy(workloads.outlier_columns(wl.wid, li, L.K, L.n_outliers)).to(dev)
+        sets = []
+        for s in range(n_sets):
+            A = torch.randn((L.M, L.K), generator=gen, device=dev, dtype=torch.float32) * wl.act_std
+            if cols.numel():
+                A[:, cols] *= wl.outlier_scale
+            G = torch.randn((L.M, L.N), generator=gen, device=dev, dtype=torch.float32) * wl.grad_std
+            sets.append((A.to(dt).contiguous(), G.to(dt).contiguous()))
+            del A, G
+        layers.append(dict(L=L, CB=CB, SCB=SCB, bias=bias, sets=sets,
+                           out=torch.empty((L.M, L.N), dtype=dt, device=dev),
+                           gA=torch.empty((L.M, L.K), dtype=dt, device=dev),
+                           gb=torch.empty((L.N,), dtype=dt, device=dev) if L.has_bias else None,
+                           wsf=I8.forward_workspace(L.M, L.K, L.K, dev),
+                           wsb=torch.empty((max(1, I8.lib.int8_linear_backward_workspace_bytes(
+                               L.M, L.N, int(L.has_bias))),), dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    return layers
+
+
+def run_gpu(wl, steps, warmup, n_sets, threshold):
+    import torch
+
+    import int8_quantized_linear_rowwise_amd as I8
+
+    layers = make_gpu_inputs(wl, n_sets)
+    nl = len(layers)
+
+    def call_fwd(ly, s):
+        A, _ = ly["sets"][s]
+        I8.int8_linear_forward(A, ly["CB"], ly["SCB"], ly["bias"], threshold, ly["L"].K, out=ly["out"],
+                               workspace=ly["wsf"])
+
+    def call_bwd(ly, s):
+        _, G = ly["sets"][s]
+        I8.int8_linear_backward_input(G, ly["CB"], ly["SCB"], with_grad_bias=ly["gb"] is not None,
+                                      grad_A=ly["gA"], grad_bias=ly["gb"], workspace=ly["wsb"])
+
+    for w in range(warmup):
+        for ly in layers:
+            call_fwd(ly, w % n_sets)
+            call_bwd(ly, w % n_sets)
+    torch.cuda.synchronize()
+    # outlier buffers never overflow (cap = K), checked once
+    for ly in layers:
+        I8.forward_check(ly["wsf"], ly["L"].M, ly["L"].K, ly["L"].K)
+
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(nl)] for _ in range(steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    t_begin.record(stream)
+    for k in range(steps):
+        s = k % n_sets
+        for li, ly in enumerate(layers):
+            e0, e1, e2 = ev[k][li]
+            e0.record(stream)
+            call_fwd(ly, s)
+            e1.record(stream)
+            call_bwd(ly, s)
+            e2.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    gpu_ms = t_begin.elapsed_time(t_end)
+    fwd_ms = [sum(ev[k][li][0].elapsed_time(ev[k][li][1]) for k in range(steps)) / steps for li in range(nl)]
+    bwd_ms = [sum(ev[k][li][1].elapsed_time(ev[k][li][2]) for k in range(steps)) / steps for li in range(nl)]
+
+    # quantizer alone (diagnostic, outside the timed region): the same rotation over
+    # every layer's activations (footprint beyond the Infinity Cache), same stream
+    dev = "cuda:0"
+    qbuf = []
+    for ly in layers:
+        L = ly["L"]
+        wsb = I8.lib.int8_quantize_rowwise_workspace_bytes(L.M, L.K)
+        qbuf.append(dict(codes=torch.empty((L.M, L.K), dtype=torch.int8, device=dev),
+                         scale=torch.empty((L.M,), dtype=torch.float32, device=dev),
+                         idx=torch.empty((L.K,), dtype=torch.int32, device=dev),
+                         cnt=torch.empty((1,), dtype=torch.int32, device=dev),
+                         sub=torch.empty((L.M, L.K), dtype=torch.float16, device=dev),
+                         ws=torch.empty((wsb,), dtype=torch.uint8, device=dev), wsb=wsb))
+    reps = 4
+    qev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+           for _ in range(reps + 1)]
+    for rr in range(reps + 1):
+        for li, ly in enumerate(layers):
+            L, qb = ly["L"], qbuf[li]
+            A2 = ly["sets"][rr % n_sets][0]
+            qev[rr][li][0].record(stream)
+            I8.check(I8.lib.int8_quantize_rowwise(A2.data_ptr(), I8.DTYPE_CODE[A2.dtype], L.M, L.K, threshold,
+                                                  qb["codes"].data_ptr(), qb["scale"].data_ptr(),
+                                                  qb["idx"].data_ptr(), qb["cnt"].data_ptr(),
+                                                  qb["sub"].data_ptr(), L.K, qb["ws"].data_ptr(), qb["wsb"],
+                                                  stream.cuda_stream), "int8_quantize_rowwise")
+            qev[rr][li][1].record(stream)
+    torch.cuda.synchronize()
+    q_ms = [sum(qev[rr][li][0].elapsed_time(qev[rr][li][1]) for rr in range(1, reps + 1)) / reps
+            for li in range(nl)]
+    del qbuf
+    return dict(layers=layers, gpu_ms=gpu_ms, host_s=h1 - h0, fwd_ms=fwd_ms, bwd_ms=bwd_ms, q_ms=q_ms)
+
+
+def cpu_baseline(wl, target_s, threshold):
+    """The oracle, untuned, on a bounded sample: every layer of the workload at a reduced token count."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    qw = []
+    for li in range(len(wl.layers)):
+        qw.append(oracle.quantize_weight(workloads.make_weight(wl, li)))
+
+    # calibrate on a small sample, then size the sample to about target_s seconds
+    def timed(Ms):
+        tt = 0.0
+        ops = 0
+        for li, L in enumerate(wl.layers):
+            A = workloads.make_activation(wl, li, rows=Ms)
+            G = workloads.make_grad(wl, li, rows=Ms)
+            b = workloads.make_bias(wl, li)
+            cb, scb = qw[li]
+            t1 = time.perf_counter()
+            oracle.linear_forward(A, wl.dtype, cb, scb, b, threshold)
+            oracle.linear_backward_input(G, wl.dtype, cb, scb)
+            if b is not None:
+                oracle.grad_bias(G, wl.dtype)
+            tt += time.perf_counter() - t1
+            ops += 4 * Ms * L.N * L.K
+        return ops, tt
+
+    Mmax = wl.layers[0].M
+    ops, tt = timed(64)
+    Ms = int(min(Mmax, max(64, 64 * target_s / max(tt, 1e-3))))
+    Ms = max(64, (Ms // 64) * 64)
+    ops, tt = timed(Ms)
+    return {"value": ops / tt / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"all {len(wl.layers)} layers of {wl.name} at {Ms} tokens (of {Mmax}): quantize + "
+                      f"forward + backward, numpy float64, {tt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_block")
+    ap.add_argument("--sets", type=int, default=2, help="rotating input sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import workloads
+    wl = workloads.WORKLOADS[args.workload]
+    threshold = wl.threshold
+    log(f"[bench] workload {wl.name}: {len(wl.layers)} layers, steps={args.steps} warmup={args.warmup}")
+    r = run_gpu(wl, args.steps, args.warmup, args.sets, threshold)
+    ms = r["gpu_ms"] / args.steps
+    ops = sum(4 * L.M * L.N * L.K for L in wl.layers)
+    tops = ops / (ms * 1e-3) / 1e12
+    bwd_flops = sum(2 * L.M * L.N * L.K for L in wl.layers)
+    bwd_ms = sum(r["bwd_ms"])
+    fwd_ms = sum(r["fwd_ms"])
+    q_ms = sum(r["q_ms"])
+    bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    fwd_gemm_ms = max(fwd_ms - q_ms, 1e-9)
+    fwd_tops = bwd_flops / (fwd_gemm_ms * 1e-3) / 1e12
+    isz = 2 if wl.dtype != "f32" else 4
+    qbytes = sum(L.M * L.K * isz + L.M * L.K + 4 * L.M + L.K for L in wl.layers)  # 1-read minimum (+ |O| terms ~0)
+    q_gbs = qbytes / (q_ms * 1e-3) / 1e9
+
+    line = {
+        "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8+fp16", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.layers[0].M,
+                   "layers": ", ".join(f"{L.name} {L.K}->{L.N}" for L in wl.layers), "io_dtype": wl.dtype,
+                   "threshold": threshold, "input_sets": args.sets},
+        "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "roofline": {"kernel": "k_gemm_bwd (memory-efficient backward grad_A)", "bound": "mfma",
+                     "achieved": round(bwd_tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_tflops / PEAK_F16_TFLOPS, 4), "traffic": None},
+        "breakdown_ms_per_step": {"forward_calls": round(fwd_ms, 4), "backward_calls": round(bwd_ms, 4),
+                                  "quantizer_alone": round(q_ms, 4), "forward_gemm_est": round(fwd_gemm_ms, 4)},
+        "per_gemm": {"fwd_int8_tops_est": round(fwd_tops, 1),
+                     "fwd_pct_int8_peak": round(100 * fwd_tops / PEAK_INT8_TOPS, 2),
+                     "bwd_fp16_tflops": round(bwd_tflops, 1),
+                     "bwd_pct_fp16_peak": round(100 * bwd_tflops / PEAK_F16_TFLOPS, 2),
+                     "quantizer_gbs_1read": round(q_gbs, 1),
+                     "quantizer_pct_hbm": round(100 * q_gbs / PEAK_HBM_GBS, 2)},
+        "host_wall_s": round(r["host_s"], 3),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, threshold)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * int8lin.h — C ABI of an LLM.int8-style row-wise quantized linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow bitsandbytes PR #33 "Memory efficient backward"
+ * (public pull request page):
+ *   - PR description: int8 weights kept row-major; forward on int8; backward
+ *     turns the int8 weights into fp16 weights on the fly and multiplies them
+ *     with the fp16 output gradient, never storing fp16 weights; inputs are
+ *     cast to fp16 and outputs back to the input dtype.
+ *   - review "Cast A to fp16" and commit "cast to half before double_quant":
+ *     the quantizer sees the fp16 cast of the activation.
+ *   - review on the bias add and "4. Mixed-precision decomposition matmul":
+ *     dequantized int8 product + bias + fp16 product of the outlier columns.
+ *   - author notes: grad_bias from the un-cast gradient; frozen weight (no
+ *     weight gradient).
+ *   - review on the backward dequantization: CB * (SCB * (1/127)).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller (the library
+ *     never allocates, frees or synchronises, except int8_linear_forward_check
+ *     which synchronises by definition). Every call only enqueues work on
+ *     `stream` (a hipStream_t passed as void*; NULL = the default stream).
+ *   - Tensors are dense and row-major (last dimension contiguous); leading
+ *     batch dimensions are flattened into the row count by the caller.
+ *   - dtype: I8L_F32, I8L_F16 or I8L_BF16 (bf16 passed as raw 16-bit words).
+ *     fp16 casts and narrowing casts round to nearest even.
+ *   - Workspaces are caller-owned device buffers of at least the size the
+ *     matching *_workspace_bytes() function returns, 256-byte aligned. Their
+ *     contents need no initialisation and are overwritten by each call.
+ *   - Return value: I8L_OK (0) or a negative error code. Argument errors are
+ *     detected on the host BEFORE any HIP call (nothing is enqueued); launch
+ *     errors are reported as I8L_EHIP. Faults inside kernels surface, as in
+ *     HIP, at the caller's next synchronisation.
+ *   - Calls are stateless and reentrant; results are bitwise deterministic.
+ *   - Outlier threshold tau: a feature column is an outlier column when any
+ *     row of the (flattened) input has |fp16(x)| > tau (strict, compared in
+ *     fp32). tau <= 0, tau = +inf or NaN disables the split.
+ */
+#ifndef INT8LIN_H
+#define INT8LIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { I8L_F32 = 0, I8L_F16 = 1, I8L_BF16 = 2 } i8l_dtype;
+
+enum {
+  I8L_OK = 0,
+  I8L_EINVAL = -1,     /* NULL pointer, negative size, misaligned workspace */
+  I8L_EDTYPE = -2,     /* dtype not one of i8l_dtype */
+  I8L_ESHAPE = -3,     /* size beyond what the kernels index, or K > I8L_MAX_K */
+  I8L_EWORKSPACE = -4, /* workspace NULL or smaller than required */
+  I8L_EHIP = -5,       /* a HIP launch or copy failed */
+  I8L_EOVERFLOW = -6   /* more outlier columns than the buffer capacity `cap` */
+};
+
+/* Largest contraction length whose int32 accumulator cannot overflow:
+ * 127 * 127 * K < 2^31. */
+#define I8L_MAX_K 133144
+
+/* Short text for an error code (static storage). */
+const char* int8_linear_strerror(int code);
+
+/* ------------------------------------------------------------------------ *
+ * Row-wise quantization (bitsandbytes PR #33: "Cast A to fp16" review, commit
+ * "cast to half before double_quant"; the 127 scale of the dequantization
+ * review). For X (rows x cols):
+ *   X16       = fp16(X)
+ *   O         = ascending outlier columns of X16 (see tau above)
+ *   s[r]      = max over c not in O of |X16[r, c]|        (0 if none)
+ *   codes     = clamp(rint(fl32(X16 * fl32(127 / s[r]))), -127, 127), 0 on O
+ *               and on rows with s[r] = 0; -128 is never produced
+ *   sub[r, j] = X16[r, O[j]] for j < min(|O|, cap)
+ * Outputs (device): codes rows x cols int8; row_scale rows fp32 (s, exact);
+ * outlier_idx cap int32 (first min(|O|, cap) entries written);
+ * outlier_count 1 int32 (= |O|, may exceed cap: overflow is then visible);
+ * sub rows x cap fp16 bits (leading dimension cap; only columns j < |O| are
+ * written). outlier_idx / sub may be NULL when cap = 0.
+ * Weights are quantized with this call and tau off: CB = codes, SCB = s.
+ * ------------------------------------------------------------------------ */
+size_t int8_quantize_rowwise_workspace_bytes(int64_t rows, int64_t cols);
+
+int int8_quantize_rowwise(const void* X, int dtype, int64_t rows, int64_t cols, float threshold,
+                          int8_t* codes, float* row_scale, int32_t* outlier_idx, int32_t* outlier_count,
+                          uint16_t* sub, int32_t cap, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Forward (bitsandbytes PR #33, review on the bias add and
+ * "4. Mixed-precision decomposition matmul"):
+ *   (CA, SCA, O, subA) = quantize(A, tau)                      (as above)
+ *   C32[m, n] = sum_k CA[m, k] * CB[n, k]                      (exact int32)
+ *   Wdq[n, k] = fp16(fl32(CB[n, k] * fl32(SCB[n] * fl32(1/127))))
+ *   out[m, n] = D(C32 * SCA[m] * SCB[n] / 127^2 + sum_j subA[m, j] * Wdq[n, O[j]]
+ *                 + bias[n])                                    (fp32 accumulate)
+ * A: M x K of `dtype`; CB: N x K int8 row-major; SCB: N fp32; bias: N of
+ * `dtype` or NULL; out: M x N of `dtype`; c32_debug: M x N int32 or NULL
+ * (exports C32). cap: capacity of the outlier buffers inside the workspace
+ * (cap >= K can never overflow). K <= I8L_MAX_K.
+ * The workspace holds the quantized activation; its layout is reported by
+ * int8_linear_forward_workspace_layout so that tests can read it back.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  size_t count;   /* int32 |O| */
+  size_t idx;     /* int32[cap] outlier columns */
+  size_t scale;   /* fp32[M] SCA */
+  size_t codes;   /* int8[M*K] CA */
+  size_t sub;     /* fp16[M*cap] subA */
+  size_t total;   /* bytes required */
+} i8l_forward_layout;
+
+size_t int8_linear_forward_workspace_bytes(int64_t M, int64_t K, int32_t cap);
+int int8_linear_forward_workspace_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* layout);
+
+int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
+                        int64_t N, const void* bias, float threshold, int32_t cap, void* out, int32_t* c32_debug,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronises `stream`, reads the outlier count of the last forward that used
+ * `workspace` and returns I8L_EOVERFLOW if it exceeded `cap` (the output of
+ * that call is then incomplete), else I8L_OK. *count receives |O| if non-NULL. */
+int int8_linear_forward_check(const void* workspace, int64_t M, int64_t K, int32_t cap, void* stream,
+                              int32_t* count);
+
+/* ------------------------------------------------------------------------ *
+ * Memory-efficient backward, input gradient only (bitsandbytes PR #33, PR
+ * description, backward-dequantization review, author notes):
+ *   grad_A[m, k]  = D(sum_n fp16(G[m, n]) * Wdq[n, k])   (fp32 accumulate)
+ *   grad_bias[n]  = D(sum_m G[m, n])   on the un-cast G    (fp32 accumulate)
+ * G: M x N of `dtype`; CB: N x K int8 row-major; SCB: N fp32; grad_A: M x K
+ * of `dtype`; grad_bias: N of `dtype` or NULL (then no workspace is needed).
+ * No weight gradient exists: the int8 weight is frozen.
+ * ------------------------------------------------------------------------ */
+size_t int8_linear_backward_workspace_bytes(int64_t M, int64_t N, int with_grad_bias);
+
+int int8_linear_backward_input(const void* G, int dtype, int64_t M, int64_t N, const int8_t* CB, const float* SCB,
+                               int64_t K, void* grad_A, void* grad_bias, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT8LIN_H */

@@ -1,0 +1,183 @@
+// C-ABI host layer: argument validation (before any HIP call), workspace
+// carving and kernel launches on the caller's stream. No allocation, no
+// synchronisation (except int8_linear_forward_check).
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/int8lin.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool valid_dtype(int dt) { return dt == I8L_F32 || dt == I8L_F16 || dt == I8L_BF16; }
+
+size_t mask_words(int64_t cols) { return (size_t)((cols + 31) / 32); }
+
+// quantizer scratch: bitmask + per-word prefix
+size_t quant_scratch_bytes(int64_t cols) {
+  const size_t nw = mask_words(cols) > 0 ? mask_words(cols) : 1;
+  return align_up(nw * 4) * 2;
+}
+
+bool fwd_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* L) {
+  if (M < 0 || K < 0 || cap < 0) return false;
+  size_t off = 0;
+  L->count = off;
+  off += ALIGN;
+  L->idx = off;
+  off += align_up((size_t)(cap > 0 ? cap : 1) * 4);
+  L->scale = off;
+  off += align_up((size_t)(M > 0 ? M : 1) * 4);
+  L->codes = off;
+  off += align_up((size_t)M * (size_t)K > 0 ? (size_t)M * (size_t)K : 1);
+  L->sub = off;
+  off += align_up((size_t)M * (size_t)cap * 2 > 0 ? (size_t)M * (size_t)cap * 2 : 2);
+  // quantizer scratch after the layout proper
+  off += quant_scratch_bytes(K);
+  L->total = off;
+  return true;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? I8L_OK : I8L_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* int8_linear_strerror(int code) {
+  switch (code) {
+    case I8L_OK: return "ok";
+    case I8L_EINVAL: return "invalid argument (NULL pointer, negative size or misaligned workspace)";
+    case I8L_EDTYPE: return "unsupported dtype";
+    case I8L_ESHAPE: return "unsupported shape (too large, or K above the int32-accumulator limit)";
+    case I8L_EWORKSPACE: return "workspace missing or too small";
+    case I8L_EHIP: return "HIP launch or copy failed";
+    case I8L_EOVERFLOW: return "more outlier columns than the outlier buffer capacity";
+    default: return "unknown error";
+  }
+}
+
+size_t int8_quantize_rowwise_workspace_bytes(int64_t rows, int64_t cols) {
+  (void)rows;
+  if (cols < 0) return 0;
+  return quant_scratch_bytes(cols);
+}
+
+int int8_quantize_rowwise(const void* X, int dtype, int64_t rows, int64_t cols, float threshold, int8_t* codes,
+                          float* row_scale, int32_t* outlier_idx, int32_t* outlier_count, uint16_t* sub,
+                          int32_t cap, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return I8L_EDTYPE;
+  if (rows < 0 || cols < 0 || cap < 0) return I8L_EINVAL;
+  if (rows > INT32_MAX || cols > INT32_MAX || rows * cols > ((int64_t)1 << 40)) return I8L_ESHAPE;
+  if (outlier_count == nullptr) return I8L_EINVAL;
+  if (rows > 0 && (row_scale == nullptr || (cols > 0 && (X == nullptr || codes == nullptr)))) return I8L_EINVAL;
+  if (cap > 0 && (outlier_idx == nullptr || (rows > 0 && sub == nullptr))) return I8L_EINVAL;
+  const size_t need = quant_scratch_bytes(cols);
+  if (ws == nullptr || ws_bytes < need) return I8L_EWORKSPACE;
+  if ((uintptr_t)ws % ALIGN) return I8L_EINVAL;
+  uint32_t* mask = static_cast<uint32_t*>(ws);
+  int32_t* prefix = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
+  return hip_status(i8l::launch_quantize(dtype, X, rows, (int)cols, threshold, codes, row_scale, outlier_idx,
+                                         outlier_count, sub, cap, mask, prefix, (hipStream_t)stream));
+}
+
+size_t int8_linear_forward_workspace_bytes(int64_t M, int64_t K, int32_t cap) {
+  i8l_forward_layout L;
+  if (!fwd_layout(M, K, cap, &L)) return 0;
+  return L.total;
+}
+
+int int8_linear_forward_workspace_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* layout) {
+  if (layout == nullptr) return I8L_EINVAL;
+  if (!fwd_layout(M, K, cap, layout)) return I8L_EINVAL;
+  return I8L_OK;
+}
+
+int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
+                        int64_t N, const void* bias, float threshold, int32_t cap, void* out, int32_t* c32,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return I8L_EDTYPE;
+  if (M < 0 || K < 0 || N < 0 || cap < 0) return I8L_EINVAL;
+  if (M > INT32_MAX || N > INT32_MAX || K > I8L_MAX_K || M * K > ((int64_t)1 << 40) ||
+      M * N > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40))
+    return I8L_ESHAPE;
+  if (M > 0 && N > 0) {
+    if (out == nullptr || SCB == nullptr) return I8L_EINVAL;
+    if (K > 0 && (A == nullptr || CB == nullptr)) return I8L_EINVAL;
+  }
+  i8l_forward_layout L;
+  fwd_layout(M, K, cap, &L);
+  if (ws == nullptr || ws_bytes < L.total) return I8L_EWORKSPACE;
+  if ((uintptr_t)ws % ALIGN) return I8L_EINVAL;
+  if (M == 0 || N == 0) return I8L_OK;
+  char* w = static_cast<char*>(ws);
+  int32_t* count = reinterpret_cast<int32_t*>(w + L.count);
+  int32_t* idx = reinterpret_cast<int32_t*>(w + L.idx);
+  float* SCA = reinterpret_cast<float*>(w + L.scale);
+  int8_t* CA = reinterpret_cast<int8_t*>(w + L.codes);
+  uint16_t* subA = reinterpret_cast<uint16_t*>(w + L.sub);
+  const size_t qs = quant_scratch_bytes(K);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(w + L.total - qs);
+  int32_t* prefix = reinterpret_cast<int32_t*>(w + L.total - qs / 2);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = i8l::launch_quantize(dtype, A, M, (int)K, threshold, CA, SCA, idx, count, subA, cap, mask,
+                                      prefix, st);
+  if (e != hipSuccess) return I8L_EHIP;
+  e = i8l::launch_gemm_fwd(dtype, CA, SCA, (int)M, CB, SCB, (int)N, (int)K, subA, cap, idx, count, bias, out, c32,
+                           st);
+  return hip_status(e);
+}
+
+int int8_linear_forward_check(const void* ws, int64_t M, int64_t K, int32_t cap, void* stream, int32_t* count) {
+  i8l_forward_layout L;
+  if (ws == nullptr || !fwd_layout(M, K, cap, &L)) return I8L_EINVAL;
+  int32_t c = 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(&c, static_cast<const char*>(ws) + L.count, sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+      hipSuccess)
+    return I8L_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return I8L_EHIP;
+  if (count) *count = c;
+  return c > cap ? I8L_EOVERFLOW : I8L_OK;
+}
+
+size_t int8_linear_backward_workspace_bytes(int64_t M, int64_t N, int with_grad_bias) {
+  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX) return 0;
+  if (!with_grad_bias) return 0;
+  return align_up(i8l::grad_bias_partial_floats((int)M, (int)N) * sizeof(float));
+}
+
+int int8_linear_backward_input(const void* G, int dtype, int64_t M, int64_t N, const int8_t* CB, const float* SCB,
+                               int64_t K, void* grad_A, void* grad_bias, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return I8L_EDTYPE;
+  if (M < 0 || N < 0 || K < 0) return I8L_EINVAL;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || M * K > ((int64_t)1 << 40) ||
+      M * N > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40))
+    return I8L_ESHAPE;
+  if (M > 0 && K > 0) {
+    if (grad_A == nullptr) return I8L_EINVAL;
+    if (N > 0 && (G == nullptr || CB == nullptr || SCB == nullptr)) return I8L_EINVAL;
+  }
+  if (grad_bias != nullptr) {
+    if (M > 0 && N > 0 && G == nullptr) return I8L_EINVAL;
+    const size_t need = int8_linear_backward_workspace_bytes(M, N, 1);
+    if (ws == nullptr || ws_bytes < need) return I8L_EWORKSPACE;
+    if ((uintptr_t)ws % ALIGN) return I8L_EINVAL;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (M > 0 && K > 0) {
+    hipError_t e = i8l::launch_gemm_bwd(dtype, G, (int)M, (int)N, CB, SCB, (int)K, grad_A, st);
+    if (e != hipSuccess) return I8L_EHIP;
+  }
+  if (grad_bias != nullptr && N > 0) {
+    hipError_t e = i8l::launch_grad_bias(dtype, G, (int)M, (int)N, static_cast<float*>(ws), grad_bias, st);
+    if (e != hipSuccess) return I8L_EHIP;
+  }
+  return I8L_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Shared device helpers for the int8 linear kernels (gfx950 / CDNA4).
+//
+// Storage dtypes: 0 = fp32, 1 = fp16, 2 = bf16 (bf16 handled as raw 16-bit
+// patterns). All conversions to fp16 and from fp32 round to nearest even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8l {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+struct bf16_t { uint16_t bits; };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite in this library;
+// NaN is kept a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Element type traits: load 8 consecutive elements as fp32 values of their
+// fp16 cast (the fp16 cast is exact for fp16 and RNE for fp32 / bf16).
+template <int DT> struct Elem;
+
+template <> struct Elem<DT_F32> {
+  typedef float T;
+  static constexpr int size = 4;
+  __device__ static __forceinline__ float to_f32(T v) { return v; }
+  __device__ static __forceinline__ T from_f32(float f) { return f; }
+};
+template <> struct Elem<DT_F16> {
+  typedef _Float16 T;
+  static constexpr int size = 2;
+  __device__ static __forceinline__ float to_f32(T v) { return (float)v; }
+  __device__ static __forceinline__ T from_f32(float f) { return (_Float16)f; }
+};
+template <> struct Elem<DT_BF16> {
+  typedef uint16_t T;
+  static constexpr int size = 2;
+  __device__ static __forceinline__ float to_f32(T v) { return bf16_to_f32(v); }
+  __device__ static __forceinline__ T from_f32(float f) { return f32_to_bf16(f); }
+};
+
+// Value of the fp16 cast of element v, as fp32 (exact).
+template <int DT>
+__device__ __forceinline__ float half_cast_f32(typename Elem<DT>::T v) {
+  if constexpr (DT == DT_F16) return (float)v;
+  else return (float)(_Float16)Elem<DT>::to_f32(v);
+}
+
+template <int DT>
+__device__ __forceinline__ _Float16 to_half(typename Elem<DT>::T v) {
+  if constexpr (DT == DT_F16) return v;
+  else return (_Float16)Elem<DT>::to_f32(v);
+}
+
+// Load 8 consecutive elements (vector load; caller guarantees alignment).
+template <int DT>
+__device__ __forceinline__ void load8(const typename Elem<DT>::T* p, typename Elem<DT>::T (&out)[8]) {
+  if constexpr (DT == DT_F32) {
+    const v4f* q = reinterpret_cast<const v4f*>(p);
+    v4f a = q[0], b = q[1];
+    out[0] = a[0]; out[1] = a[1]; out[2] = a[2]; out[3] = a[3];
+    out[4] = b[0]; out[5] = b[1]; out[6] = b[2]; out[7] = b[3];
+  } else {
+    v4u a = *reinterpret_cast<const v4u*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w = a[i];
+      uint16_t lo = (uint16_t)(w & 0xffffu), hi = (uint16_t)(w >> 16);
+      out[2 * i] = __builtin_bit_cast(typename Elem<DT>::T, lo);
+      out[2 * i + 1] = __builtin_bit_cast(typename Elem<DT>::T, hi);
+    }
+  }
+}
+
+__device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+// Wave-wide reductions (wave64).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace i8l

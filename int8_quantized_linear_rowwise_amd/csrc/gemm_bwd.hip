@@ -1,0 +1,340 @@
+// Memory-efficient backward of the int8 linear layer on gfx950 matrix cores.
+//
+// bitsandbytes PR #33 "Memory efficient backward", PR description and the
+// review on the backward dequantization (CB cast, multiplied by
+// SCB * (1/127)): the row-major int8 weights are turned into fp16 weights on
+// the fly and multiplied with the fp16 output gradient; no fp16 weights are
+// stored. The weight is frozen, so only the input gradient is produced:
+//   grad_A[m, k] = D( sum_n fp16(G[m, n]) * Wdq[n, k] ),
+//   Wdq[n, k]    = fp16( CB[n, k] * fl32(SCB[n] * fl32(1/127)) ).
+// The contraction runs along the rows of CB (the strided direction), so each
+// int8 tile of CB is dequantized once per workgroup while it is staged into
+// LDS, transposed to n-contiguous fp16 rows that feed v_mfma_f32_32x32x16_f16
+// directly. The output is computed transposed (weights on the MFMA's row side)
+// so that each lane owns four consecutive k of one token.
+//
+// Author notes of the same PR: grad_bias comes from the un-cast gradient; it
+// is a column sum of G in fp32, accumulated in a fixed order (deterministic).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace i8l {
+
+__device__ __forceinline__ int xcd_remap_b(int pid, int nt) {
+  const int x = pid & 7, i = pid >> 3;
+  const int base = nt >> 3, rem = nt & 7;
+  return x * base + (x < rem ? x : rem) + i;
+}
+
+template <int BM, int BK, int BNC, int DT, bool GV, bool WV, bool OV>
+__global__ __launch_bounds__(256) void k_gemm_bwd(const typename Elem<DT>::T* __restrict__ G, int M, int N,
+                                                  const int8_t* __restrict__ CB, const float* __restrict__ SCB,
+                                                  int K, typename Elem<DT>::T* __restrict__ gA) {
+  typedef typename Elem<DT>::T T;
+  constexpr int LDN = BNC + 8;                 // halfs per LDS row (padded)
+  constexpr int WK = BK / 2, WM = BM / 2;
+  constexpr int TI = WK / 32, TJ = WM / 32;
+  constexpr int GCPR = BNC / 8;                // 8-element chunks per G row
+  constexpr int GCPT = BM * GCPR / 256;        // G chunks per thread
+  constexpr int KQ = BK / 4;                   // 4-byte k quads per CB row of the tile
+  constexpr int UPT = (BNC / 8) * KQ / 256;    // 8(n) x 4(k) CB units per thread
+  static_assert(GCPT * 256 == BM * GCPR && UPT * 256 == (BNC / 8) * KQ, "tile/thread mismatch");
+
+  extern __shared__ __attribute__((aligned(16))) _Float16 hsm[];
+  _Float16* sW = hsm;                          // [2][BK][LDN]  (k rows, n contiguous)
+  _Float16* sG = hsm + 2 * BK * LDN;           // [2][BM][LDN]  (m rows, n contiguous)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int wk = wave & 1, wm = wave >> 1;
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_k = (K + BK - 1) / BK;
+  const int nt = tiles_m * tiles_k;
+  const int pid = xcd_remap_b(blockIdx.x, nt);
+  constexpr int GRP = 8;
+  const int group = pid / (GRP * tiles_k);
+  const int first_m = group * GRP;
+  const int gsz = min(tiles_m - first_m, GRP);
+  const int tm = first_m + (pid % (GRP * tiles_k)) % gsz;
+  const int tk = (pid % (GRP * tiles_k)) / gsz;
+  const int m0 = tm * BM, k0 = tk * BK;
+
+  // prefetch registers (raw storage words: 4 per 8-element chunk for 16-bit
+  // types, 8 for fp32)
+  constexpr int GW = (DT == DT_F32) ? 8 : 4;
+  uint32_t graw[GCPT][GW];
+  uint32_t wraw[UPT][8];
+  float wsig[UPT][8];
+
+  auto gload = [&](int nc) {
+#pragma unroll
+    for (int i = 0; i < GCPT; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / GCPR, col = (c % GCPR) * 8;
+      const int m = m0 + row, n = nc + col;
+      const T* src = G + (int64_t)m * N + n;
+      if (GV) {
+        if (m < M && n < N) {
+          if constexpr (DT == DT_F32) {
+            v4u a = *reinterpret_cast<const v4u*>(src);
+            v4u b = *reinterpret_cast<const v4u*>(src + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { graw[i][e] = a[e]; graw[i][e + 4] = b[e]; }
+          } else {
+            v4u a = *reinterpret_cast<const v4u*>(src);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) graw[i][e] = a[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < GW; ++e) graw[i][e] = 0u;
+        }
+      } else {
+        if constexpr (DT == DT_F32) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            graw[i][e] = (m < M && n + e < N) ? __float_as_uint(src[e]) : 0u;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t lo = (m < M && n + 2 * e < N) ? (uint32_t)__builtin_bit_cast(uint16_t, src[2 * e]) : 0u;
+            uint32_t hi = (m < M && n + 2 * e + 1 < N) ? (uint32_t)__builtin_bit_cast(uint16_t, src[2 * e + 1]) : 0u;
+            graw[i][e] = lo | (hi << 16);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int un = tid + 256 * u;
+      const int kq = un % KQ, ng = un / KQ;
+      const int k = k0 + 4 * kq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int n = nc + 8 * ng + e;
+        uint32_t w = 0u;
+        float s = 0.0f;
+        if (n < N) {
+          s = SCB[n] * (1.0f / 127.0f);
+          const int8_t* p = CB + (int64_t)n * K + k;
+          if (WV) {
+            if (k < K) w = *reinterpret_cast<const uint32_t*>(p);
+          } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              if (k + b < K) w |= ((uint32_t)(uint8_t)p[b]) << (8 * b);
+          }
+        }
+        wraw[u][e] = w;
+        wsig[u][e] = s;
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+    _Float16* dG = sG + buf * BM * LDN;
+#pragma unroll
+    for (int i = 0; i < GCPT; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / GCPR, col = (c % GCPR) * 8;
+      v8h h;
+      if constexpr (DT == DT_F16) {
+        h = __builtin_bit_cast(v8h, v4u{graw[i][0], graw[i][1], graw[i][2], graw[i][3]});
+      } else if constexpr (DT == DT_BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[2 * e] = (_Float16)__uint_as_float(graw[i][e] << 16);
+          h[2 * e + 1] = (_Float16)__uint_as_float(graw[i][e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)__uint_as_float(graw[i][e]);
+      }
+      *reinterpret_cast<v8h*>(dG + row * LDN + col) = h;
+    }
+    _Float16* dW = sW + buf * BK * LDN;
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int un = tid + 256 * u;
+      const int kq = un % KQ, ng = un / KQ;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v8h h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int b = (int)(int8_t)(wraw[u][e] >> (8 * c));
+          h[e] = (_Float16)((float)b * wsig[u][e]);
+        }
+        *reinterpret_cast<v8h*>(dW + (4 * kq + c) * LDN + 8 * ng) = h;
+      }
+    }
+  };
+
+  v16f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
+
+  const int nn = (N + BNC - 1) / BNC;
+  if (nn > 0) {
+    gload(0);
+    sstore(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < nn; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < nn) gload((t + 1) * BNC);
+    const _Float16* bW = sW + cur * BK * LDN + (wk * WK + lr) * LDN + lg * 8;
+    const _Float16* bG = sG + cur * BM * LDN + (wm * WM + lr) * LDN + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < BNC / 16; ++ks) {
+      v8h P[TI], Q[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) P[i] = *reinterpret_cast<const v8h*>(bW + i * 32 * LDN + ks * 16);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) Q[j] = *reinterpret_cast<const v8h*>(bG + j * 32 * LDN + ks * 16);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P[i], Q[j], acc[i][j], 0, 0, 0);
+    }
+    if (t + 1 < nn) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // lane (lr, lg), register r of tile (i, j):
+  //   k = k0 + wk*WK + i*32 + (r/4)*8 + lg*4 + r%4,  m = m0 + wm*WM + j*32 + lr
+  const int kb = k0 + wk * WK + lg * 4;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int m = m0 + wm * WM + j * 32 + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = kb + i * 32 + q * 8;
+        T* p = gA + (int64_t)m * K + k;
+        T v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = Elem<DT>::from_f32(acc[i][j][4 * q + e]);
+        if (OV && k + 3 < K) {
+          if constexpr (DT == DT_F32) {
+            *reinterpret_cast<v4f*>(p) = v4f{v[0], v[1], v[2], v[3]};
+          } else {
+            v2u w;
+            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
+            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
+            *reinterpret_cast<v2u*>(p) = w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (k + e < K) p[e] = v[e];
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BK, int BNC, int DT, bool GV, bool WV, bool OV>
+static hipError_t launch_bwd_cfg(const void* G, int M, int N, const int8_t* CB, const float* SCB, int K, void* gA,
+                                 hipStream_t st) {
+  typedef typename Elem<DT>::T T;
+  constexpr int LDN = BNC + 8;
+  constexpr size_t lds = (size_t)2 * (BK + BM) * LDN * sizeof(_Float16);
+  auto kern = k_gemm_bwd<BM, BK, BNC, DT, GV, WV, OV>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles = ((M + BM - 1) / BM) * ((K + BK - 1) / BK);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, static_cast<const T*>(G), M, N, CB, SCB, K,
+                     static_cast<T*>(gA));
+  return hipGetLastError();
+}
+
+template <int DT, bool GV, bool WV, bool OV>
+static hipError_t launch_bwd_dt(const void* G, int M, int N, const int8_t* CB, const float* SCB, int K, void* gA,
+                                hipStream_t st) {
+  const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((K + 255) / 256);
+  if (big_tiles >= 200) return launch_bwd_cfg<256, 256, 64, DT, GV, WV, OV>(G, M, N, CB, SCB, K, gA, st);
+  return launch_bwd_cfg<128, 128, 64, DT, GV, WV, OV>(G, M, N, CB, SCB, K, gA, st);
+}
+
+hipError_t launch_gemm_bwd(int dt, const void* G, int M, int N, const int8_t* CB, const float* SCB, int K,
+                           void* gA, hipStream_t st) {
+  const int esz = dt == DT_F32 ? 4 : 2;
+  const bool gv = (N % 8 == 0) && ((uintptr_t)G % 16 == 0);
+  const bool wv = (K % 4 == 0) && ((uintptr_t)CB % 4 == 0);
+  const bool ov = (K % 4 == 0) && ((uintptr_t)gA % (4 * esz) == 0);
+#define I8L_BWD(D)                                                                   \
+  do {                                                                               \
+    if (gv && wv && ov) return launch_bwd_dt<D, true, true, true>(G, M, N, CB, SCB, K, gA, st); \
+    return launch_bwd_dt<D, false, false, false>(G, M, N, CB, SCB, K, gA, st);      \
+  } while (0)
+  switch (dt) {
+    case DT_F32: I8L_BWD(DT_F32);
+    case DT_F16: I8L_BWD(DT_F16);
+    default: I8L_BWD(DT_BF16);
+  }
+#undef I8L_BWD
+}
+
+// ---------------------------------------------------------------------------
+// grad_bias: column sums of the un-cast gradient.
+
+constexpr int GB_ROWS = 128;   // rows per partial
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_colsum_partial(const typename Elem<DT>::T* __restrict__ G, int M, int N,
+                                                        float* __restrict__ partial) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int r0 = blockIdx.y * GB_ROWS;
+  const int r1 = min(M, r0 + GB_ROWS);
+  float s = 0.0f;
+  for (int r = r0; r < r1; ++r) s += Elem<DT>::to_f32(G[(int64_t)r * N + n]);
+  partial[(int64_t)blockIdx.y * N + n] = s;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_colsum_final(const float* __restrict__ partial, int nparts, int N,
+                                                      typename Elem<DT>::T* __restrict__ gb) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.0f;
+  for (int p = 0; p < nparts; ++p) s += partial[(int64_t)p * N + n];
+  gb[n] = Elem<DT>::from_f32(s);
+}
+
+size_t grad_bias_partial_floats(int M, int N) {
+  const int64_t parts = (M + GB_ROWS - 1) / GB_ROWS;
+  return (size_t)(parts < 1 ? 1 : parts) * (size_t)(N < 1 ? 1 : N);
+}
+
+template <int DT>
+static hipError_t launch_gb_t(const void* G, int M, int N, float* partial, void* gb, hipStream_t st) {
+  typedef typename Elem<DT>::T T;
+  if (N <= 0) return hipSuccess;
+  const int parts = (M + GB_ROWS - 1) / GB_ROWS;
+  if (parts > 0)
+    hipLaunchKernelGGL(k_colsum_partial<DT>, dim3((N + 255) / 256, parts), dim3(256), 0, st,
+                       static_cast<const T*>(G), M, N, partial);
+  hipLaunchKernelGGL(k_colsum_final<DT>, dim3((N + 255) / 256), dim3(256), 0, st, partial, parts, N,
+                     static_cast<T*>(gb));
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_bias(int dt, const void* G, int M, int N, float* partial, void* gb, hipStream_t st) {
+  switch (dt) {
+    case DT_F32: return launch_gb_t<DT_F32>(G, M, N, partial, gb, st);
+    case DT_F16: return launch_gb_t<DT_F16>(G, M, N, partial, gb, st);
+    default: return launch_gb_t<DT_BF16>(G, M, N, partial, gb, st);
+  }
+}
+
+}  // namespace i8l

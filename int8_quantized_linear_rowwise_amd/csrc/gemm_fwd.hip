@@ -1,0 +1,331 @@
+// Forward of the int8 linear layer on gfx950 matrix cores.
+//
+// bitsandbytes PR #33 "Memory efficient backward", review on _functions.py
+// (dequantize, cast, add bias; "4. Mixed-precision decomposition matmul"):
+//   y[m, n] = C32[m, n] * SCA[m] * SCB[n] / 127^2
+//             + sum_j subA[m, j] * Wdq[n, O[j]]       (fp16 x fp16 -> fp32)
+//             + bias[n]
+//   out = D(y)
+// with C32 = CA . CB^T exact in int32, CA (M x K) and CB (N x K) both int8
+// row-major (K contiguous), and Wdq[n, k] = fp16(CB[n, k] * (SCB[n] * (1/127)))
+// rebuilt from the int8 weights (no fp16 weights are kept).
+//
+// One kernel: LDS-staged int8 tiles, double buffered through registers, fed
+// to v_mfma_i32_32x32x32_i8; the int32 accumulators are dequantized in
+// registers, the outlier product runs on v_mfma_f32_32x32x16_f16 into the
+// same fp32 accumulators, then bias, cast and store. The product is computed
+// as C^T (weights on the MFMA's row side) so that each lane owns four
+// consecutive output features of one token and stores them as one vector.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace i8l {
+
+__device__ __forceinline__ int xcd_remap(int pid, int nt) {
+  // Workgroups are handed to the 8 XCDs round-robin; give each XCD one
+  // contiguous run of tile ids so neighbouring tiles share that XCD's L2.
+  const int x = pid & 7, i = pid >> 3;
+  const int base = nt >> 3, rem = nt & 7;
+  return x * base + (x < rem ? x : rem) + i;
+}
+
+template <int BM, int BN, int BK, int DT, bool KV, bool OV>
+__global__ __launch_bounds__(256) void k_gemm_fwd(const int8_t* __restrict__ CA, const float* __restrict__ SCA,
+                                                  int M, const int8_t* __restrict__ CB,
+                                                  const float* __restrict__ SCB, int N, int K,
+                                                  const uint16_t* __restrict__ subA, int cap,
+                                                  const int32_t* __restrict__ idx,
+                                                  const int32_t* __restrict__ count,
+                                                  const typename Elem<DT>::T* __restrict__ bias,
+                                                  typename Elem<DT>::T* __restrict__ out,
+                                                  int32_t* __restrict__ c32) {
+  typedef typename Elem<DT>::T T;
+  constexpr int LDK = BK + 16;           // padded row pitch (bytes): conflict-free 16-byte reads
+  constexpr int WN = BN / 2, WM = BM / 2;
+  constexpr int TI = WN / 32, TJ = WM / 32;
+  constexpr int CPR = BK / 16;           // 16-byte chunks per tile row
+  constexpr int NCB = BN * CPR, NCA = BM * CPR;
+  constexpr int CPT = (NCB + NCA) / 256; // chunks per thread per stage
+  static_assert((NCB % 256) == 0 && (NCA % 256) == 0, "tile/thread mismatch");
+
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+  int8_t* sB = smem;                      // [2][BN][LDK]
+  int8_t* sA = smem + 2 * BN * LDK;       // [2][BM][LDK]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int wn = wave & 1, wm = wave >> 1;
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int nt = tiles_m * tiles_n;
+  int pid = xcd_remap(blockIdx.x, nt);
+  constexpr int GRP = 8;
+  const int group = pid / (GRP * tiles_n);
+  const int first_m = group * GRP;
+  const int gsz = min(tiles_m - first_m, GRP);
+  const int tm = first_m + (pid % (GRP * tiles_n)) % gsz;
+  const int tn = (pid % (GRP * tiles_n)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  v4i pre[CPT];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const bool isB = c < NCB;
+      const int cc = isB ? c : c - NCB;
+      const int row = cc / CPR, col = (cc % CPR) * 16;
+      const int grow = (isB ? n0 : m0) + row;
+      const int lim = isB ? N : M;
+      const int8_t* base = isB ? CB : CA;
+      const int k = kt + col;
+      v4i v = {0, 0, 0, 0};
+      if (grow < lim) {
+        const int8_t* p = base + (int64_t)grow * K + k;
+        if constexpr (KV) {
+          if (k < K) v = *reinterpret_cast<const v4i*>(p);
+        } else {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int b = 0; b < 16; ++b)
+            if (k + b < K) w[b >> 2] |= ((uint32_t)(uint8_t)p[b]) << (8 * (b & 3));
+          v = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        }
+      }
+      pre[i] = v;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const bool isB = c < NCB;
+      const int cc = isB ? c : c - NCB;
+      const int row = cc / CPR, col = (cc % CPR) * 16;
+      int8_t* dst = (isB ? sB + buf * BN * LDK : sA + buf * BM * LDK) + row * LDK + col;
+      *reinterpret_cast<v4i*>(dst) = pre[i];
+    }
+  };
+
+  v16i acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
+
+  const int nk = (K + BK - 1) / BK;
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const int8_t* bB = sB + cur * BN * LDK + (wn * WN + lr) * LDK + lg * 16;
+    const int8_t* bA = sA + cur * BM * LDK + (wm * WM + lr) * LDK + lg * 16;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      v4i P[TI], Q[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) P[i] = *reinterpret_cast<const v4i*>(bB + i * 32 * LDK + ks * 32);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) Q[j] = *reinterpret_cast<const v4i*>(bA + j * 32 * LDK + ks * 32);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(P[i], Q[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------- epilogue ----------------
+  // lane (lr, lg), register r of tile (i, j):
+  //   n = n0 + wn*WN + i*32 + (r/4)*8 + lg*4 + r%4,  m = m0 + wm*WM + j*32 + lr
+  const int nb = n0 + wn * WN + lg * 4;
+  const int mb = m0 + wm * WM + lr;
+
+  if (c32 != nullptr) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int m = mb + j * 32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb + i * 32 + q * 8;
+          int32_t* p = c32 + (int64_t)m * N + n;
+          if (OV && n + 3 < N) {
+            *reinterpret_cast<v4i*>(p) = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                             acc[i][j][4 * q + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) p[e] = acc[i][j][4 * q + e];
+          }
+        }
+      }
+  }
+
+  float sa[TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int m = mb + j * 32;
+    sa[j] = (m < M) ? SCA[m] : 0.0f;
+  }
+  v16f accf[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    float sb[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
+      sb[r] = (n < N) ? SCB[n] : 0.0f;
+    }
+    // (SCA * SCB) * fl32(1/127^2): exactly 1 when both scales are 127
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        accf[i][j][r] = (float)acc[i][j][r] * ((sa[j] * sb[r]) * (1.0f / 16129.0f));
+  }
+
+  // outlier columns: fp16 product accumulated into the same fp32 registers
+  int cnt = 0;
+  if (count != nullptr) {
+    cnt = *count;
+    if (cnt > cap) cnt = cap;
+  }
+  for (int jo = 0; jo < cnt; jo += 16) {
+    v8h P[TI], Q[TJ];
+    int kk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = jo + lg * 8 + e;
+      kk[e] = (j < cnt) ? idx[j] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int n = n0 + wn * WN + i * 32 + lr;
+      const bool nok = n < N;
+      const float sig = nok ? SCB[n] * (1.0f / 127.0f) : 0.0f;
+      const int8_t* wrow = CB + (int64_t)(nok ? n : 0) * K;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        P[i][e] = (nok && kk[e] >= 0) ? (_Float16)((float)wrow[kk[e]] * sig) : (_Float16)0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = m0 + wm * WM + j * 32 + lr;
+      const bool mok = m < M;
+      const uint16_t* srow = subA + (int64_t)(mok ? m : 0) * cap;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jj = jo + lg * 8 + e;
+        Q[j][e] = (mok && jj < cnt) ? __builtin_bit_cast(_Float16, srow[jj]) : (_Float16)0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P[i], Q[j], accf[i][j], 0, 0, 0);
+  }
+
+  // bias, cast, store
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    float bv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
+      bv[r] = (bias != nullptr && n < N) ? Elem<DT>::to_f32(bias[n]) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = mb + j * 32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb + i * 32 + q * 8;
+        T* p = out + (int64_t)m * N + n;
+        T v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = Elem<DT>::from_f32(accf[i][j][4 * q + e] + bv[4 * q + e]);
+        if (OV && n + 3 < N) {
+          if constexpr (DT == DT_F32) {
+            *reinterpret_cast<v4f*>(p) = v4f{v[0], v[1], v[2], v[3]};
+          } else {
+            v2u w;
+            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
+            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
+            *reinterpret_cast<v2u*>(p) = w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) p[e] = v[e];
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int DT, bool KV, bool OV>
+static hipError_t launch_fwd_cfg(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
+                                 int N, int K, const uint16_t* subA, int cap, const int32_t* idx,
+                                 const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
+  typedef typename Elem<DT>::T T;
+  constexpr int LDK = BK + 16;
+  constexpr size_t lds = (size_t)2 * (BM + BN) * LDK;
+  auto kern = k_gemm_fwd<BM, BN, BK, DT, KV, OV>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count,
+                     static_cast<const T*>(bias), static_cast<T*>(out), c32);
+  return hipGetLastError();
+}
+
+template <int DT, bool KV, bool OV>
+static hipError_t launch_fwd_dt(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
+                                int N, int K, const uint16_t* subA, int cap, const int32_t* idx, const int32_t* count,
+                                const void* bias, void* out, int32_t* c32, hipStream_t st) {
+  const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 200)
+    return launch_fwd_cfg<256, 256, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out,
+                                                    c32, st);
+  return launch_fwd_cfg<128, 128, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32,
+                                                  st);
+}
+
+hipError_t launch_gemm_fwd(int dt, const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
+                           int N, int K, const uint16_t* subA, int cap, const int32_t* idx, const int32_t* count,
+                           const void* bias, void* out, int32_t* c32, hipStream_t st) {
+  const bool kv = (K % 16 == 0) && ((uintptr_t)CA % 16 == 0) && ((uintptr_t)CB % 16 == 0);
+  const int osz = dt == DT_F32 ? 4 : 2;
+  const bool ov = (N % 4 == 0) && ((uintptr_t)out % (4 * osz) == 0) && (c32 == nullptr || (uintptr_t)c32 % 16 == 0);
+#define I8L_FWD(D, A, B) \
+  return launch_fwd_dt<D, A, B>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st)
+  switch (dt) {
+    case DT_F32:
+      if (kv) { if (ov) I8L_FWD(DT_F32, true, true); else I8L_FWD(DT_F32, true, false); }
+      else { if (ov) I8L_FWD(DT_F32, false, true); else I8L_FWD(DT_F32, false, false); }
+    case DT_F16:
+      if (kv) { if (ov) I8L_FWD(DT_F16, true, true); else I8L_FWD(DT_F16, true, false); }
+      else { if (ov) I8L_FWD(DT_F16, false, true); else I8L_FWD(DT_F16, false, false); }
+    default:
+      if (kv) { if (ov) I8L_FWD(DT_BF16, true, true); else I8L_FWD(DT_BF16, true, false); }
+      else { if (ov) I8L_FWD(DT_BF16, false, true); else I8L_FWD(DT_BF16, false, false); }
+  }
+#undef I8L_FWD
+}
+
+}  // namespace i8l

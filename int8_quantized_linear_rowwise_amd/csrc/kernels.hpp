@@ -1,0 +1,30 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8l {
+
+// Quantizer: X (rows x cols, dtype dt) -> codes, scale, outlier list (first
+// `cap` entries), count, sub (rows x cap fp16). mask / prefix: ceil(cols/32)
+// words each of scratch.
+hipError_t launch_quantize(int dt, const void* X, int64_t rows, int cols, float tau, int8_t* codes, float* scale,
+                           int32_t* idx, int32_t* count, uint16_t* sub, int cap, uint32_t* mask,
+                           int32_t* prefix, hipStream_t st);
+
+// Forward GEMM with fused epilogue: out = D(CA.CB^T * SCA SCB / 127^2
+// + subA . Wdq[:, idx]^T + bias); optional int32 export of CA.CB^T.
+hipError_t launch_gemm_fwd(int dt, const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
+                           int N, int K, const uint16_t* subA, int cap, const int32_t* idx, const int32_t* count,
+                           const void* bias, void* out, int32_t* c32, hipStream_t st);
+
+// Backward-input GEMM: grad_A = D(fp16(G) . Wdq), Wdq built from CB on the fly.
+hipError_t launch_gemm_bwd(int dt, const void* G, int M, int N, const int8_t* CB, const float* SCB, int K,
+                           void* grad_A, hipStream_t st);
+
+// grad_bias[n] = D(sum_m G[m, n]) (fp32 accumulation, fixed order).
+size_t grad_bias_partial_floats(int M, int N);
+hipError_t launch_grad_bias(int dt, const void* G, int M, int N, float* partial, void* grad_bias, hipStream_t st);
+
+}  // namespace i8l

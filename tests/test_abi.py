@@ -1,0 +1,152 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every
+function the header declares, and rejects bad arguments on the host before
+any HIP call (so nothing here touches a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "int8lin.h")
+LIB = os.path.join(ROOT, "int8_quantized_linear_rowwise_amd", "libint8lin.so")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        from int8_quantized_linear_rowwise_amd import build
+        build.build(verbose=False)
+    from int8_quantized_linear_rowwise_amd import _lib
+    return _lib
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(int8_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared()
+    for n in ("int8_quantize_rowwise", "int8_linear_forward", "int8_linear_backward_input"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    cdll = ctypes.CDLL(LIB)
+    for n in _declared():
+        assert hasattr(cdll, n), n
+    # the binding describes exactly the declared set
+    assert set(L.SIGNATURES) == set(_declared())
+
+
+def test_exports_are_plain_c(L):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in _declared():
+        assert n in syms, n          # unmangled
+
+
+def test_strerror(L):
+    for c in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert isinstance(L.lib.int8_linear_strerror(c), bytes)
+    assert L.lib.int8_linear_strerror(-4).startswith(b"workspace")
+
+
+FAKE = 1 << 20   # a non-NULL, 256-aligned address that is never dereferenced
+
+
+def test_quantize_host_errors(L):
+    f = L.lib.int8_quantize_rowwise
+    ws = L.lib.int8_quantize_rowwise_workspace_bytes(4, 64)
+    args = dict(X=FAKE, dt=1, R=4, C=64, tau=6.0, codes=FAKE, scale=FAKE, idx=FAKE, cnt=FAKE, sub=FAKE, cap=64,
+                ws=FAKE, wsb=ws, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["X"], a["dt"], a["R"], a["C"], a["tau"], a["codes"], a["scale"], a["idx"], a["cnt"], a["sub"],
+                 a["cap"], a["ws"], a["wsb"], a["st"])
+
+    assert call(dt=3) == L.I8L_EDTYPE
+    assert call(dt=-1) == L.I8L_EDTYPE
+    assert call(R=-1) == L.I8L_EINVAL
+    assert call(C=-5) == L.I8L_EINVAL
+    assert call(cap=-1) == L.I8L_EINVAL
+    assert call(X=0) == L.I8L_EINVAL
+    assert call(codes=0) == L.I8L_EINVAL
+    assert call(scale=0) == L.I8L_EINVAL
+    assert call(cnt=0) == L.I8L_EINVAL
+    assert call(idx=0) == L.I8L_EINVAL
+    assert call(sub=0) == L.I8L_EINVAL
+    assert call(ws=0) == L.I8L_EWORKSPACE
+    assert call(wsb=ws - 1) == L.I8L_EWORKSPACE
+    assert call(ws=FAKE + 8) == L.I8L_EINVAL
+    assert call(R=1 << 33) == L.I8L_ESHAPE
+
+
+def test_forward_host_errors(L):
+    f = L.lib.int8_linear_forward
+    M, K, N, cap = 8, 64, 32, 64
+    ws = L.lib.int8_linear_forward_workspace_bytes(M, K, cap)
+    base = dict(A=FAKE, dt=1, M=M, K=K, CB=FAKE, SCB=FAKE, N=N, bias=0, tau=6.0, cap=cap, out=FAKE, c32=0, ws=FAKE,
+                wsb=ws, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["A"], a["dt"], a["M"], a["K"], a["CB"], a["SCB"], a["N"], a["bias"], a["tau"], a["cap"],
+                 a["out"], a["c32"], a["ws"], a["wsb"], a["st"])
+
+    assert call(dt=7) == L.I8L_EDTYPE
+    assert call(M=-1) == L.I8L_EINVAL
+    assert call(K=-1) == L.I8L_EINVAL
+    assert call(N=-1) == L.I8L_EINVAL
+    assert call(cap=-1) == L.I8L_EINVAL
+    assert call(A=0) == L.I8L_EINVAL
+    assert call(CB=0) == L.I8L_EINVAL
+    assert call(SCB=0) == L.I8L_EINVAL
+    assert call(out=0) == L.I8L_EINVAL
+    assert call(K=L.I8L_MAX_K + 1) == L.I8L_ESHAPE
+    assert call(ws=0) == L.I8L_EWORKSPACE
+    assert call(wsb=ws - 1) == L.I8L_EWORKSPACE
+    assert call(ws=FAKE + 16) == L.I8L_EINVAL
+    # empty problems succeed without touching the device
+    assert call(M=0, wsb=L.lib.int8_linear_forward_workspace_bytes(0, K, cap)) == L.I8L_OK
+    assert call(N=0) == L.I8L_OK
+
+
+def test_backward_host_errors(L):
+    f = L.lib.int8_linear_backward_input
+    M, N, K = 8, 32, 64
+    ws = L.lib.int8_linear_backward_workspace_bytes(M, N, 1)
+    base = dict(G=FAKE, dt=2, M=M, N=N, CB=FAKE, SCB=FAKE, K=K, gA=FAKE, gb=FAKE, ws=FAKE, wsb=ws, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["G"], a["dt"], a["M"], a["N"], a["CB"], a["SCB"], a["K"], a["gA"], a["gb"], a["ws"], a["wsb"],
+                 a["st"])
+
+    assert call(dt=5) == L.I8L_EDTYPE
+    assert call(M=-2) == L.I8L_EINVAL
+    assert call(G=0) == L.I8L_EINVAL
+    assert call(CB=0) == L.I8L_EINVAL
+    assert call(SCB=0) == L.I8L_EINVAL
+    assert call(gA=0) == L.I8L_EINVAL
+    assert call(ws=0) == L.I8L_EWORKSPACE
+    assert call(wsb=ws - 1) == L.I8L_EWORKSPACE
+    assert call(M=1 << 32) == L.I8L_ESHAPE
+    assert L.lib.int8_linear_backward_workspace_bytes(M, N, 0) == 0
+
+
+def test_forward_layout(L):
+    for (M, K, cap) in [(1, 1, 0), (600, 4, 4), (2048, 4096, 4096), (16384, 28672, 28672), (5, 70, 3)]:
+        lay = L.ForwardLayout()
+        assert L.lib.int8_linear_forward_workspace_layout(M, K, cap, lay) == 0
+        offs = [lay.count, lay.idx, lay.scale, lay.codes, lay.sub]
+        sizes = [4, 4 * cap, 4 * M, M * K, 2 * M * cap]
+        assert all(o % 256 == 0 for o in offs)
+        for (o, s), o2 in zip(zip(offs, sizes), offs[1:] + [lay.total]):
+            assert o + s <= o2
+        assert lay.total == L.lib.int8_linear_forward_workspace_bytes(M, K, cap)
+    assert L.lib.int8_linear_forward_workspace_layout(-1, 4, 4, L.ForwardLayout()) == L.I8L_EINVAL

@@ -1,0 +1,327 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Integer results (codes, row scales as bits, outlier lists and counts, the
+fp16 outlier sub-matrix, int32 accumulators, int8 weights) must match bit
+for bit; float results must meet bitsandbytes PR #33's test bounds against
+the oracle's float64 value plus a tight ulp bound. Sizes here span several
+tiles with ragged tails; the full workload sizes are in test_gpu_workloads.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._gpu import TORCH, assert_bits_equal, assert_float_gate, dev, host
+
+pytestmark = pytest.mark.gpu
+
+DTS = ["f16", "bf16", "f32"]
+
+
+@pytest.fixture(scope="module")
+def I8():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import int8_quantized_linear_rowwise_amd as I8
+    return I8
+
+
+def _quant_case(dt, R, C, seed, n_out=3, scale=20.0):
+    g = np.random.default_rng(np.random.SeedSequence([7, R, C, seed]))
+    x = g.standard_normal((R, C)).astype(np.float32)
+    if n_out and C:
+        cols = g.choice(C, min(n_out, C), replace=False)
+        x[:, cols] *= np.float32(scale)
+    return workloads._store(x, dt)
+
+
+def _check_quant(I8, X, dt, tau, cap=None):
+    R, C = X.shape
+    codes, scale, idx, cnt, sub = I8.int8_quantize_rowwise(dev(X, dt), tau, cap)
+    torch.cuda.synchronize()
+    q = oracle.quantize_rowwise(X, dt, tau)
+    n = int(host(cnt)[0])
+    assert n == q["outliers"].size, (n, q["outliers"].size)
+    capn = C if cap is None else cap
+    k = min(n, capn)
+    assert_bits_equal(host(codes), q["codes"], "codes")
+    assert_bits_equal(host(scale), q["scale"], "row scale")
+    assert_bits_equal(host(idx)[:k], q["outliers"][:k], "outlier index list")
+    assert_bits_equal(host(sub)[:, :k], q["sub"][:, :k], "outlier sub-matrix")
+    return q
+
+
+QSHAPES = [(1, 1), (3, 7), (17, 70), (64, 4096), (129, 4104), (5, 8200), (33, 11008), (2, 40000),
+           (600, 4), (600, 16), (1000, 64)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("R,C", QSHAPES)
+def test_quantize_bit_exact(I8, dt, R, C):
+    X = _quant_case(dt, R, C, 0)
+    for tau in (6.0, 0.0, float("inf")):
+        _check_quant(I8, X, dt, tau)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_quantize_edge_cases(I8, dt):
+    # ties at the threshold (6.0 is not an outlier), zero rows, rows with only outliers
+    X = np.zeros((6, 40), np.float32)
+    X[1, 3] = 6.0
+    X[2, :] = 1.0
+    X[2, 5] = 6.0078125
+    X[3, 5] = 7.0
+    X[4, 10] = -6.5
+    X[4, 11] = 0.25
+    X = workloads._store(X, dt)
+    q = _check_quant(I8, X, dt, 6.0)
+    assert q["outliers"].tolist() == [5, 10]
+    # all-outlier input (tiny threshold), and a threshold below every value
+    Y = _quant_case(dt, 9, 33, 1, n_out=0)
+    q = _check_quant(I8, Y, dt, 1e-6)
+    assert q["outliers"].size == 33
+    # fp16-subnormal magnitudes
+    g = np.random.default_rng(9)
+    z = g.standard_normal((8, 48)).astype(np.float32) * np.float32(2.0 ** -20)
+    _check_quant(I8, workloads._store(z, dt), dt, 6.0)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_quantize_cap_overflow_visible(I8, dt):
+    X = _quant_case(dt, 20, 64, 3, n_out=5)
+    q = _check_quant(I8, X, dt, 6.0, cap=2)
+    assert q["outliers"].size >= 5
+
+
+# --------------------------------------------------------------------------
+# forward / backward at sizes spanning several tiles
+
+
+LSHAPES = [(1, 64, 1), (33, 70, 45), (130, 200, 260), (257, 4096, 300), (64, 16, 4), (600, 4, 16),
+           (300, 1040, 520), (513, 256, 1031)]
+
+
+def _layer(dt, M, K, N, seed, n_out=4, bias=True):
+    c = workloads.small_case(dt, M, K, N, seed, n_outliers=min(n_out, K), has_bias=bias)
+    return c["A"], c["W"], c["bias"], c["G"]
+
+
+def _gpu_weights(I8, W):
+    CB, SCB = I8.quantize_weight(dev(W))
+    return CB, SCB
+
+
+def _check_weights(I8, W):
+    CB, SCB = _gpu_weights(I8, W)
+    torch.cuda.synchronize()
+    cb, scb = oracle.quantize_weight(W)
+    assert_bits_equal(host(CB), cb, "CB")
+    assert_bits_equal(host(SCB), scb, "SCB")
+    return CB, SCB, cb, scb
+
+
+def _forward_and_check(I8, A, dt, CB, SCB, cb, scb, bias, tau, cap=None, rows=None):
+    M, K = A.shape
+    N = cb.shape[0]
+    capn = K if cap is None else cap
+    ws = I8.forward_workspace(M, K, capn, "cuda:0")
+    c32 = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
+    out = I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(bias, dt) if bias is not None else None, tau, capn,
+                                 c32=c32, workspace=ws)
+    torch.cuda.synchronize()
+    f = oracle.linear_forward(A, dt, cb, scb, bias, tau, rows=rows)
+    q = f["q"]
+    # the forward's own quantization, read back from its workspace
+    L = I8.forward_layout(M, K, capn)
+    wsh = host(ws)
+    cnt = int(wsh[L.count:L.count + 4].view(np.int32)[0])
+    assert cnt == q["outliers"].size
+    k = min(cnt, capn)
+    assert_bits_equal(wsh[L.idx:L.idx + 4 * k].view(np.int32), q["outliers"][:k], "forward outlier list")
+    assert_bits_equal(wsh[L.scale:L.scale + 4 * M].view(np.float32), q["scale"], "SCA")
+    assert_bits_equal(wsh[L.codes:L.codes + M * K].view(np.int8).reshape(M, K), q["codes"], "CA")
+    if capn:
+        subw = wsh[L.sub:L.sub + 2 * M * capn].view(np.float16).reshape(M, capn)[:, :k]
+        assert_bits_equal(subw, q["sub"][:, :k], "subA")
+    idx = f["rows"]
+    assert_bits_equal(host(c32)[idx], f["c32"].astype(np.int32), "C32")
+    assert_float_gate(host(out)[idx], dt, f["y"], "out")
+    return out, f
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("M,K,N", LSHAPES)
+def test_forward_parity(I8, dt, M, K, N):
+    A, W, b, _ = _layer(dt, M, K, N, 1)
+    CB, SCB, cb, scb = _check_weights(I8, W)
+    _forward_and_check(I8, A, dt, CB, SCB, cb, scb, b, 6.0)
+    _forward_and_check(I8, A, dt, CB, SCB, cb, scb, None, float("inf"))
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("M,K,N", LSHAPES)
+def test_backward_parity(I8, dt, M, K, N):
+    _, W, _, G = _layer(dt, M, K, N, 2)
+    CB, SCB, cb, scb = _check_weights(I8, W)
+    gA, gb = I8.int8_linear_backward_input(dev(G, dt), CB, SCB, with_grad_bias=True)
+    torch.cuda.synchronize()
+    r = oracle.linear_backward_input(G, dt, cb, scb)
+    assert_float_gate(host(gA), dt, r["y"], "grad_A")
+    gb64, _ = oracle.grad_bias(G, dt)
+    assert_float_gate(host(gb), dt, gb64, "grad_bias", tight_rel=2.0 ** -16)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_forward_zero_input_is_bias_bitwise(I8, dt):
+    M, K, N = 70, 96, 130
+    _, W, b, _ = _layer(dt, M, K, N, 3)
+    CB, SCB = _gpu_weights(I8, W)
+    A = workloads._store(np.zeros((M, K), np.float32), dt)
+    out = I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt), 6.0)
+    assert_bits_equal(host(out), np.broadcast_to(b, (M, N)).copy(), "out == bias")
+
+
+def _int_weights(g, N, K):
+    W = g.integers(-127, 128, (N, K)).astype(np.float32)
+    W[np.arange(N), g.integers(0, K, N)] = np.where(g.random(N) < 0.5, -127, 127)
+    return W
+
+
+def test_forward_integer_case_exact(I8):
+    g = np.random.default_rng(50)
+    M, K, N = 150, 320, 140
+    A = _int_weights(g, M, K)
+    W = _int_weights(g, N, K)
+    CB, SCB = _gpu_weights(I8, W)
+    c32 = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
+    out = I8.int8_linear_forward(dev(A), CB, SCB, None, float("inf"), c32=c32)
+    ref = A.astype(np.int64) @ W.astype(np.int64).T
+    assert_bits_equal(host(c32), ref.astype(np.int32), "C32 textbook")
+    assert np.array_equal(host(out).astype(np.float64), ref.astype(np.float64))
+
+
+def test_forward_all_outliers(I8):
+    g = np.random.default_rng(51)
+    M, K, N = 90, 72, 50
+    A = (g.uniform(0.5, 2, (M, K)) * np.where(g.random((M, K)) < .5, -1, 1)).astype(np.float16)
+    W = _int_weights(g, N, K)
+    CB, SCB = _gpu_weights(I8, W)
+    b = (g.standard_normal(N) * 0.01).astype(np.float16)
+    out = I8.int8_linear_forward(dev(A), CB, SCB, dev(b), 1e-3)
+    ref = A.astype(np.float64) @ W.astype(np.float64).T + b.astype(np.float64)
+    assert_float_gate(host(out), "f16", ref, "all-outlier out")
+
+
+def test_backward_integer_case_exact(I8):
+    g = np.random.default_rng(52)
+    M, N, K = 200, 300, 260
+    W = _int_weights(g, N, K)
+    CB, SCB = _gpu_weights(I8, W)
+    G = g.integers(-1, 2, (M, N)).astype(np.float32)
+    gA, _ = I8.int8_linear_backward_input(dev(G), CB, SCB, with_grad_bias=False)
+    ref = G.astype(np.int64) @ W.astype(np.int64)
+    assert np.array_equal(host(gA), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_forward_outlier_overflow_reported(I8, dt):
+    M, K, N = 40, 64, 32
+    A, W, b, _ = _layer(dt, M, K, N, 4, n_out=6)
+    CB, SCB = _gpu_weights(I8, W)
+    ws = I8.forward_workspace(M, K, 2, "cuda:0")
+    I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt), 6.0, cap=2, workspace=ws)
+    with pytest.raises(I8.Int8LinError) as e:
+        I8.forward_check(ws, M, K, 2)
+    assert e.value.code == -6
+    ws2 = I8.forward_workspace(M, K, K, "cuda:0")
+    I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt), 6.0, cap=K, workspace=ws2)
+    assert I8.forward_check(ws2, M, K, K) >= 6
+
+
+def test_empty_and_degenerate(I8):
+    CB, SCB = _gpu_weights(I8, np.ones((8, 16), np.float32))
+    A = torch.zeros((0, 16), dtype=torch.float16, device="cuda:0")
+    assert I8.int8_linear_forward(A, CB, SCB).shape == (0, 8)
+    G = torch.zeros((0, 8), dtype=torch.float16, device="cuda:0")
+    gA, gb = I8.int8_linear_backward_input(G, CB, SCB)
+    torch.cuda.synchronize()
+    assert gA.shape == (0, 16) and np.all(host(gb) == 0)
+    # K = 0: out = bias
+    CB0 = torch.zeros((8, 0), dtype=torch.int8, device="cuda:0")
+    SCB0 = torch.zeros((8,), dtype=torch.float32, device="cuda:0")
+    b = torch.arange(8, dtype=torch.float16, device="cuda:0")
+    out = I8.int8_linear_forward(torch.zeros((5, 0), dtype=torch.float16, device="cuda:0"), CB0, SCB0, b)
+    assert np.array_equal(host(out), np.broadcast_to(host(b), (5, 8)))
+
+
+def test_rejects_cpu_tensors(I8):
+    with pytest.raises(ValueError):
+        I8.int8_linear_forward(torch.zeros((2, 16)), torch.zeros((4, 16), dtype=torch.int8),
+                               torch.zeros(4))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_determinism_ten_runs(I8, dt):
+    """bitsandbytes PR #33 ran every test ten times for stability: outputs must be bitwise identical."""
+    M, K, N = 520, 1100, 700
+    A, W, b, G = _layer(dt, M, K, N, 5)
+    CB, SCB = _gpu_weights(I8, W)
+    At, bt, Gt = dev(A, dt), dev(b, dt), dev(G, dt)
+    ref = None
+    for _ in range(10):
+        out = I8.int8_linear_forward(At, CB, SCB, bt, 6.0)
+        gA, gb = I8.int8_linear_backward_input(Gt, CB, SCB)
+        cur = (host(out), host(gA), host(gb))
+        if ref is None:
+            ref = cur
+        else:
+            for a, r, w in zip(cur, ref, ("out", "grad_A", "grad_bias")):
+                assert_bits_equal(a, r, w)
+
+
+# --------------------------------------------------------------------------
+# autograd glue and the residual MLP of the EasyDeL example
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_autograd_module_matches_c_calls(I8, dt):
+    M, K, N = 96, 200, 72
+    A, W, b, G = _layer(dt, M, K, N, 6)
+    lin = I8.Int8Linear(dev(W), dev(b, dt).float()).cuda()
+    x = dev(A, dt).reshape(2, 48, K).requires_grad_(True)
+    y = lin(x)
+    y.backward(dev(G, dt).reshape(2, 48, N))
+    out = I8.int8_linear_forward(dev(A, dt), lin.CB, lin.SCB, lin.bias.detach().to(TORCH[dt]), 6.0)
+    gA, gb = I8.int8_linear_backward_input(dev(G, dt), lin.CB, lin.SCB)
+    assert_bits_equal(host(y.detach().reshape(M, N)), host(out), "module out")
+    assert_bits_equal(host(x.grad.reshape(M, K)), host(gA), "module grad_A")
+    assert_bits_equal(host(lin.bias.grad.to(TORCH[dt])), host(gb), "module grad_bias")
+
+
+def test_mlp600_residual_example(I8):
+    wl = workloads.WORKLOADS["mlp600"]
+    x = workloads.make_activation(wl, 0)
+    g = workloads.make_grad(wl, 1)
+    Ws = [workloads.make_weight(wl, i) for i in range(2)]
+    bs = [workloads.make_bias(wl, i) for i in range(2)]
+    layers = []
+    for W, b in zip(Ws, bs):
+        cb, s = oracle.quantize_weight(W)
+        layers.append((cb, s, b))
+    r = oracle.mlp_forward_backward(x, g, "f32", layers, wl.threshold)
+    # GPU: int8 linears from the library; SiLU and the residual add as torch glue
+    gw = [_gpu_weights(I8, W) for W in Ws]
+    xt, gt = dev(x), dev(g)
+    h = I8.int8_linear_forward(xt, gw[0][0], gw[0][1], dev(bs[0]), wl.threshold)
+    a = torch.nn.functional.silu(h)
+    o = I8.int8_linear_forward(a, gw[1][0], gw[1][1], dev(bs[1]), wl.threshold) + xt
+    ga, gb2 = I8.int8_linear_backward_input(gt, gw[1][0], gw[1][1])
+    sg = torch.sigmoid(h)
+    gh = ga * sg * (1 + h * (1 - sg))
+    gx, gb1 = I8.int8_linear_backward_input(gh, gw[0][0], gw[0][1])
+    gx = gx + gt
+    torch.cuda.synchronize()
+    assert_float_gate(host(o), "f32", oracle.to_f64(r["out"], "f32"), "mlp out", tight_rel=2.0 ** -8)
+    assert_float_gate(host(gx), "f32", oracle.to_f64(r["grad_x"], "f32"), "mlp grad_x", tight_rel=2.0 ** -8)
+    # the second layer's quantizer on the oracle's own SiLU output is bit-exact
+    _check_quant(I8, r["a"], "f32", wl.threshold)

@@ -1,0 +1,82 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: every layer of every workload.
+
+Bit-exact over the whole tensors: int8 weights and scales, the forward's
+quantized activation (codes, row scales, outlier list and count, fp16
+outlier sub-matrix). On sampled rows (first, last and random ones), which
+the oracle computes one by one: int32 accumulators (bit-exact), forward
+output and input gradient (pages' bounds + tight ulp bound). grad_bias is
+checked whole.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._gpu import assert_bits_equal, assert_float_gate, dev, host
+
+pytestmark = pytest.mark.gpu
+
+CASES = [(name, li) for name in workloads.WORKLOAD_ORDER if name != "mlp600"
+         for li in range(len(workloads.WORKLOADS[name].layers))]
+
+
+def _rows(M, n=24, seed=0):
+    g = np.random.default_rng(seed)
+    r = set(g.choice(M, min(n, M), replace=False).tolist()) | {0, M - 1}
+    return np.array(sorted(r))
+
+
+@pytest.fixture(scope="module")
+def I8():
+    assert torch.cuda.is_available()
+    import int8_quantized_linear_rowwise_amd as I8
+    return I8
+
+
+@pytest.mark.parametrize("name,li", CASES, ids=[f"{n}-{workloads.WORKLOADS[n].layers[i].name}" for n, i in CASES])
+def test_workload_layer(I8, name, li):
+    wl = workloads.WORKLOADS[name]
+    L = wl.layers[li]
+    dt, tau = wl.dtype, wl.threshold
+    print(f"\n[{name}/{L.name}] M={L.M} K={L.K} N={L.N} dt={dt}", flush=True)
+    W = workloads.make_weight(wl, li)
+    CB, SCB = I8.quantize_weight(dev(W))
+    cb, scb = oracle.quantize_weight(W)
+    assert_bits_equal(host(CB), cb, "CB")
+    assert_bits_equal(host(SCB), scb, "SCB")
+    del W
+    A = workloads.make_activation(wl, li)
+    b = workloads.make_bias(wl, li)
+    M, K, N = L.M, L.K, L.N
+    ws = I8.forward_workspace(M, K, K, "cuda:0")
+    c32 = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
+    out = I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt) if b is not None else None, tau, K, c32=c32,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    rows = _rows(M)
+    f = oracle.linear_forward(A, dt, cb, scb, b, tau, rows=rows)
+    q = f["q"]
+    lay = I8.forward_layout(M, K, K)
+    cnt = int(host(ws[lay.count:lay.count + 4]).view(np.int32)[0])
+    assert cnt == q["outliers"].size
+    seeded = workloads.outlier_columns(wl.wid, li, K, L.n_outliers)
+    assert set(seeded.tolist()) <= set(q["outliers"].tolist())
+    assert_bits_equal(host(ws[lay.idx:lay.idx + 4 * cnt]).view(np.int32), q["outliers"], "outlier list")
+    assert_bits_equal(host(ws[lay.scale:lay.scale + 4 * M]).view(np.float32), q["scale"], "SCA")
+    assert_bits_equal(host(ws[lay.codes:lay.codes + M * K]).view(np.int8).reshape(M, K), q["codes"], "CA")
+    subw = host(ws[lay.sub:lay.sub + 2 * M * K]).view(np.float16).reshape(M, K)[:, :cnt]
+    assert_bits_equal(subw, q["sub"], "subA")
+    rt = torch.from_numpy(rows).to("cuda:0")
+    assert_bits_equal(host(c32.index_select(0, rt)), f["c32"].astype(np.int32), "C32 (sampled rows)")
+    assert_float_gate(host(out.index_select(0, rt)), dt, f["y"], "out (sampled rows)")
+    del A, c32, out, ws, f, q
+    G = workloads.make_grad(wl, li)
+    gA, gb = I8.int8_linear_backward_input(dev(G, dt), CB, SCB, with_grad_bias=b is not None)
+    torch.cuda.synchronize()
+    r = oracle.linear_backward_input(G, dt, cb, scb, rows=rows)
+    assert_float_gate(host(gA.index_select(0, rt)), dt, r["y"], "grad_A (sampled rows)")
+    if b is not None:
+        gb64, _ = oracle.grad_bias(G, dt)
+        assert_float_gate(host(gb), dt, gb64, "grad_bias", tight_rel=2.0 ** -16)

@@ -94,6 +94,42 @@ __device__ __forceinline__ void load8(const typename Elem<DT>::T* p, typename El
 
 __device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 
+// LDS tiles of 128-byte rows are stored with their eight 16-byte chunks
+// permuted: chunk c of row r lives at position c ^ lds_swz(r). For 16-byte
+// accesses by consecutive rows (operand fragment reads) or by eight lanes
+// sharing a row (tile writes) the positions hit distinct bank groups, with
+// either 32 or 64 four-byte banks. lds_swz depends only on r mod 32, so row
+// offsets that are multiples of 32 fold into instruction immediates.
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+
+// Buffer resource for raw (byte-addressed) buffer loads: reads at offsets
+// beyond num_bytes return zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes, 0x00020000);
+}
+constexpr int OOB_OFFSET = 0x7ffffff0;
+
+#define I8L_SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+enum : int { SG_MFMA = 0x008, SG_VMEM_R = 0x020, SG_DS_R = 0x100, SG_DS_W = 0x200, SG_VALU = 0x002 };
+
+// Output-tile order. Workgroups are handed to the 8 XCDs round-robin; each
+// XCD gets one contiguous run of tile ids (so neighbouring tiles share that
+// XCD's L2), and within a run tiles go down groups of 8 row-tiles before
+// moving to the next column-tile, so concurrently running workgroups share
+// operand tiles.
+__device__ __forceinline__ void tile_coords(int bid, int tiles_r, int tiles_c, int& tr, int& tc) {
+  const int nt = tiles_r * tiles_c;
+  const int x = bid & 7, i = bid >> 3;
+  const int base = nt >> 3, rem = nt & 7;
+  const int pid = x * base + (x < rem ? x : rem) + i;
+  constexpr int GRP = 8;
+  const int group = pid / (GRP * tiles_c);
+  const int first = group * GRP;
+  const int gsz = min(tiles_r - first, GRP);
+  tr = first + (pid % (GRP * tiles_c)) % gsz;
+  tc = (pid % (GRP * tiles_c)) / gsz;
+}
+
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -20,11 +20,6 @@
 
 namespace i8l {
 
-__device__ __forceinline__ int xcd_remap_b(int pid, int nt) {
-  const int x = pid & 7, i = pid >> 3;
-  const int base = nt >> 3, rem = nt & 7;
-  return x * base + (x < rem ? x : rem) + i;
-}
 
 template <int BM, int BK, int BNC, int DT, bool GV, bool WV, bool OV>
 __global__ __launch_bounds__(256) void k_gemm_bwd(const typename Elem<DT>::T* __restrict__ G, int M, int N,
@@ -49,14 +44,8 @@ __global__ __launch_bounds__(256) void k_gemm_bwd(const typename Elem<DT>::T* __
   const int wk = wave & 1, wm = wave >> 1;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_k = (K + BK - 1) / BK;
-  const int nt = tiles_m * tiles_k;
-  const int pid = xcd_remap_b(blockIdx.x, nt);
-  constexpr int GRP = 8;
-  const int group = pid / (GRP * tiles_k);
-  const int first_m = group * GRP;
-  const int gsz = min(tiles_m - first_m, GRP);
-  const int tm = first_m + (pid % (GRP * tiles_k)) % gsz;
-  const int tk = (pid % (GRP * tiles_k)) / gsz;
+  int tm, tk;
+  tile_coords(blockIdx.x, tiles_m, tiles_k, tm, tk);
   const int m0 = tm * BM, k0 = tk * BK;
 
   // prefetch registers (raw storage words: 4 per 8-element chunk for 16-bit
@@ -238,6 +227,257 @@ __global__ __launch_bounds__(256) void k_gemm_bwd(const typename Elem<DT>::T* __
   }
 }
 
+// Large-tile backward kernel for 16-bit gradients: 256 (m) x 256 (k) output
+// tile, 4 waves of 128 x 128, the contraction over n stepped 64 at a time
+// through two swizzled LDS stages of 64 KB (W^T tile: 256 k-rows x 64 n,
+// G tile: 256 m-rows x 64 n, both fp16). Per stage each wave runs 64 MFMAs;
+// the next stage's int8 weights and gradient come in through buffer loads at
+// the start of the stage and are dequantized / converted and written to the
+// other LDS stage in the following phases, interleaved with the MFMAs.
+// Requires N % 8 == 0 and K % 4 == 0.
+template <int DT, bool OV>
+__global__ __launch_bounds__(256, 1) void k_gemm_bwd_big(const typename Elem<DT>::T* __restrict__ G, int M, int N,
+                                                         const int8_t* __restrict__ CB,
+                                                         const float* __restrict__ SCB, int K,
+                                                         typename Elem<DT>::T* __restrict__ gA) {
+  static_assert(DT == DT_F16 || DT == DT_BF16, "16-bit gradients only");
+  constexpr int BM = 256, BK = 256, BNC = 64, TI = 4, TJ = 4;
+  constexpr int ROW = BNC * 2;                 // bytes per LDS row
+  constexpr int STAGE = (BK + BM) * ROW;       // 64 KB
+  constexpr int GOFF = BK * ROW;               // G tile after the W^T tile
+  extern __shared__ __attribute__((aligned(16))) char bsm[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lg = lane >> 5;
+  const int wk = wave & 1, wm = wave >> 1;
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_k = (K + BK - 1) / BK;
+  int tm, tk;
+  tile_coords(blockIdx.x, tiles_m, tiles_k, tm, tk);
+  const int m0 = tm * BM, k0 = tk * BK;
+
+  const __amdgpu_buffer_rsrc_t rG = make_rsrc(G + (int64_t)m0 * N, min(BM, M - m0) * N * 2);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(CB + k0, N * K - k0);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(SCB, N * 4);
+
+  // G slots: 16-byte chunk gc of rows grow + 32 i
+  const int grow = tid >> 3, gc = tid & 7;
+  const int gvoff = grow * N * 2 + 16 * gc;
+  const int gwoff = GOFF + grow * ROW + 16 * (gc ^ lds_swz(grow));
+  // W units: 8 consecutive n (wave-uniform group) x 4 consecutive k (per lane)
+  const int kq = tid & 63;
+  const int wvoff = 4 * kq;
+  int wwoff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) wwoff[c] = (4 * kq + c) * ROW;
+
+  const int sw = lds_swz(lr);
+  int roff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) roff[ks] = lr * ROW + 16 * ((2 * ks + lg) ^ sw);
+  const int pb = wk * 128 * ROW, qb = GOFF + wm * 128 * ROW;
+
+  v4u RG[8];
+  uint32_t RW[2][8];
+  float SG[2][8];
+
+  auto gload = [&](int nc) {
+    // weights first: they are converted first
+    // Rows n >= N lie past the end of the buffer and read as zero. Columns
+    // k >= K of the last tile read the next row's bytes: they only reach
+    // output columns k >= K, which are never stored.
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int n8 = nc + 8 * (wave + 4 * u);      // wave-uniform; N % 8 == 0
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        RW[u][e] = __builtin_amdgcn_raw_buffer_load_b32(rW, (n8 + e) * K + wvoff, 0, 0);
+      const int so = (n8 < N) ? 4 * n8 : OOB_OFFSET;
+      const v4f s0 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rS, so, 0, 0));
+      const v4f s1 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rS, so + 16, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        SG[u][e] = s0[e];
+        SG[u][4 + e] = s1[e];
+      }
+    }
+    // chunks past N (contraction tail) must read as zero: push them out of range
+    const int keep = -(int)(nc + 8 * gc < N);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int oi = ((gvoff + 2 * nc + 32 * i * N * 2) & keep) | (OOB_OFFSET & ~keep);
+      RG[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rG, oi, 0, 0));
+    }
+  };
+  auto wwrite = [&](int st, int u) {
+    const int ng = wave + 4 * u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v8h h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int b = (int)(int8_t)(RW[u][e] >> (8 * c));
+        h[e] = (_Float16)((float)b * (SG[u][e] * (1.0f / 127.0f)));
+      }
+      const int r = 4 * kq + c;
+      *reinterpret_cast<v8h*>(bsm + st * STAGE + wwoff[c] + 16 * (ng ^ lds_swz(r))) = h;
+    }
+  };
+  auto gwrite = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v8h h;
+      if constexpr (DT == DT_F16) {
+        h = __builtin_bit_cast(v8h, RG[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[2 * e] = (_Float16)__uint_as_float(RG[i][e] << 16);
+          h[2 * e + 1] = (_Float16)__uint_as_float(RG[i][e] & 0xffff0000u);
+        }
+      }
+      *reinterpret_cast<v8h*>(bsm + st * STAGE + gwoff + i * 32 * ROW) = h;
+    }
+  };
+
+  v16f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
+
+  v8h F[2][8];
+  auto fread = [&](int st, int ks, int b) {
+    const char* base = bsm + st * STAGE + roff[ks];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) F[b][i] = *reinterpret_cast<const v8h*>(base + pb + i * 32 * ROW);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) F[b][4 + j] = *reinterpret_cast<const v8h*>(base + qb + j * 32 * ROW);
+  };
+  auto mma = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F[b][i], F[b][4 + j], acc[i][j], 0, 0, 0);
+  };
+
+  const int nn = (N + BNC - 1) / BNC;
+  gload(0);
+  wwrite(0, 0);
+  wwrite(0, 1);
+  gwrite(0);
+  __syncthreads();
+  fread(0, 0, 0);
+  for (int t = 0; t < nn; ++t) {
+    const int st = t & 1;
+    gload((t + 1) * BNC);            // past the end: zeros
+    fread(st, 1, 1);
+    mma(0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_DS_R, 1);
+      I8L_SGB(SG_VMEM_R, 3);
+    }
+    I8L_SGB(SG_MFMA, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    fread(st, 2, 0);
+    wwrite(st ^ 1, 0);
+    mma(1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_DS_R, 1);
+      I8L_SGB(SG_VALU, 5);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_VALU, 5);
+      I8L_SGB(SG_DS_W, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    fread(st, 3, 1);
+    wwrite(st ^ 1, 1);
+    mma(0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_DS_R, 1);
+      I8L_SGB(SG_VALU, 5);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_VALU, 5);
+      I8L_SGB(SG_DS_W, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    gwrite(st ^ 1);
+    mma(1);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_VALU, 6);
+      I8L_SGB(SG_DS_W, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    fread(st ^ 1, 0, 0);
+  }
+
+  // lane (lr, lg), register r of tile (i, j):
+  //   k = k0 + wk*128 + i*32 + (r/4)*8 + lg*4 + r%4,  m = m0 + wm*128 + j*32 + lr
+  typedef typename Elem<DT>::T T;
+  const int kb = k0 + wk * 128 + lg * 4;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int m = m0 + wm * 128 + j * 32 + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = kb + i * 32 + q * 8;
+        T* p = gA + (int64_t)m * K + k;
+        T v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = Elem<DT>::from_f32(acc[i][j][4 * q + e]);
+        if (OV && k + 3 < K) {
+          v2u w;
+          w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
+          w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
+          *reinterpret_cast<v2u*>(p) = w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (k + e < K) p[e] = v[e];
+        }
+      }
+    }
+  }
+}
+
+template <int DT, bool OV>
+static hipError_t launch_bwd_big(const void* G, int M, int N, const int8_t* CB, const float* SCB, int K, void* gA,
+                                 hipStream_t st) {
+  typedef typename Elem<DT>::T T;
+  constexpr size_t lds = (size_t)2 * (256 + 256) * 128;
+  auto kern = k_gemm_bwd_big<DT, OV>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles = ((M + 255) / 256) * ((K + 255) / 256);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, static_cast<const T*>(G), M, N, CB, SCB, K,
+                     static_cast<T*>(gA));
+  return hipGetLastError();
+}
+
 template <int BM, int BK, int BNC, int DT, bool GV, bool WV, bool OV>
 static hipError_t launch_bwd_cfg(const void* G, int M, int N, const int8_t* CB, const float* SCB, int K, void* gA,
                                  hipStream_t st) {
@@ -260,8 +500,6 @@ static hipError_t launch_bwd_cfg(const void* G, int M, int N, const int8_t* CB, 
 template <int DT, bool GV, bool WV, bool OV>
 static hipError_t launch_bwd_dt(const void* G, int M, int N, const int8_t* CB, const float* SCB, int K, void* gA,
                                 hipStream_t st) {
-  const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((K + 255) / 256);
-  if (big_tiles >= 200) return launch_bwd_cfg<256, 256, 64, DT, GV, WV, OV>(G, M, N, CB, SCB, K, gA, st);
   return launch_bwd_cfg<128, 128, 64, DT, GV, WV, OV>(G, M, N, CB, SCB, K, gA, st);
 }
 
@@ -271,6 +509,14 @@ hipError_t launch_gemm_bwd(int dt, const void* G, int M, int N, const int8_t* CB
   const bool gv = (N % 8 == 0) && ((uintptr_t)G % 16 == 0);
   const bool wv = (K % 4 == 0) && ((uintptr_t)CB % 4 == 0);
   const bool ov = (K % 4 == 0) && ((uintptr_t)gA % (4 * esz) == 0);
+  // the large-tile kernel addresses its operands with 32-bit buffer offsets
+  const bool fits = ((int64_t)N + 128) * K < ((int64_t)1 << 31) - 4096 &&
+                    (int64_t)N * 2 * 256 < ((int64_t)1 << 31) - 4096;
+  const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((K + 255) / 256);
+  if (dt != DT_F32 && gv && wv && ov && fits && big_tiles >= 64) {
+    if (dt == DT_F16) return launch_bwd_big<DT_F16, true>(G, M, N, CB, SCB, K, gA, st);
+    return launch_bwd_big<DT_BF16, true>(G, M, N, CB, SCB, K, gA, st);
+  }
 #define I8L_BWD(D)                                                                   \
   do {                                                                               \
     if (gv && wv && ov) return launch_bwd_dt<D, true, true, true>(G, M, N, CB, SCB, K, gA, st); \

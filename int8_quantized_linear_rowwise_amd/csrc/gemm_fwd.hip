@@ -21,12 +21,136 @@
 
 namespace i8l {
 
-__device__ __forceinline__ int xcd_remap(int pid, int nt) {
-  // Workgroups are handed to the 8 XCDs round-robin; give each XCD one
-  // contiguous run of tile ids so neighbouring tiles share that XCD's L2.
-  const int x = pid & 7, i = pid >> 3;
-  const int base = nt >> 3, rem = nt & 7;
-  return x * base + (x < rem ? x : rem) + i;
+
+// Fused epilogue shared by the forward kernels. A wave owns TI x TJ tiles of
+// 32 x 32 (n x m); lane (lr, lg) holds, for tile (i, j) and register r,
+//   n = nw + i*32 + (r/4)*8 + lg*4 + r%4,   m = mw + j*32 + lr.
+template <int TI, int TJ, int DT, bool OV>
+__device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw, int lr, int lg, int M, int N, int K,
+                                             const float* __restrict__ SCA, const int8_t* __restrict__ CB,
+                                             const float* __restrict__ SCB, const uint16_t* __restrict__ subA,
+                                             int cap, const int32_t* __restrict__ idx,
+                                             const int32_t* __restrict__ count,
+                                             const typename Elem<DT>::T* __restrict__ bias,
+                                             typename Elem<DT>::T* __restrict__ out, int32_t* __restrict__ c32) {
+  typedef typename Elem<DT>::T T;
+  const int nb = nw + lg * 4;
+  const int mb = mw + lr;
+
+  if (c32 != nullptr) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int m = mb + j * 32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb + i * 32 + q * 8;
+          int32_t* p = c32 + (int64_t)m * N + n;
+          if (OV && n + 3 < N) {
+            *reinterpret_cast<v4i*>(p) = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                             acc[i][j][4 * q + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) p[e] = acc[i][j][4 * q + e];
+          }
+        }
+      }
+  }
+
+  float sa[TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int m = mb + j * 32;
+    sa[j] = (m < M) ? SCA[m] : 0.0f;
+  }
+  int cnt = 0;
+  if (count != nullptr) {
+    cnt = *count;
+    if (cnt > cap) cnt = cap;
+  }
+
+  // one slab of TJ tiles (32 output features) at a time keeps the fp32 copy small
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    float sb[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
+      sb[r] = (n < N) ? SCB[n] : 0.0f;
+    }
+    // (SCA * SCB) * fl32(1/127^2): exactly 1 when both scales are 127
+    v16f accf[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        accf[j][r] = (float)acc[i][j][r] * ((sa[j] * sb[r]) * (1.0f / 16129.0f));
+
+    // outlier columns: fp16 product accumulated into the same fp32 registers
+    for (int jo = 0; jo < cnt; jo += 16) {
+      v8h P, Q[TJ];
+      const int n = nw + i * 32 + lr;
+      const bool nok = n < N;
+      const float sig = nok ? SCB[n] * (1.0f / 127.0f) : 0.0f;
+      const int8_t* wrow = CB + (int64_t)(nok ? n : 0) * K;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jj = jo + lg * 8 + e;
+        P[e] = (nok && jj < cnt) ? (_Float16)((float)wrow[idx[jj]] * sig) : (_Float16)0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int m = mw + j * 32 + lr;
+        const bool mok = m < M;
+        const uint16_t* srow = subA + (int64_t)(mok ? m : 0) * cap;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int jj = jo + lg * 8 + e;
+          Q[j][e] = (mok && jj < cnt) ? __builtin_bit_cast(_Float16, srow[jj]) : (_Float16)0.0f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) accf[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P, Q[j], accf[j], 0, 0, 0);
+    }
+
+    // bias, cast, store
+    float bv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
+      bv[r] = (bias != nullptr && n < N) ? Elem<DT>::to_f32(bias[n]) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = mb + j * 32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb + i * 32 + q * 8;
+        T* p = out + (int64_t)m * N + n;
+        T v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = Elem<DT>::from_f32(accf[j][4 * q + e] + bv[4 * q + e]);
+        if (OV && n + 3 < N) {
+          if constexpr (DT == DT_F32) {
+            *reinterpret_cast<v4f*>(p) = v4f{v[0], v[1], v[2], v[3]};
+          } else {
+            v2u w;
+            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
+            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
+            *reinterpret_cast<v2u*>(p) = w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) p[e] = v[e];
+        }
+      }
+    }
+  }
 }
 
 template <int BM, int BN, int BK, int DT, bool KV, bool OV>
@@ -57,14 +181,8 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(const int8_t* __restrict__ CA,
   const int wn = wave & 1, wm = wave >> 1;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int nt = tiles_m * tiles_n;
-  int pid = xcd_remap(blockIdx.x, nt);
-  constexpr int GRP = 8;
-  const int group = pid / (GRP * tiles_n);
-  const int first_m = group * GRP;
-  const int gsz = min(tiles_m - first_m, GRP);
-  const int tm = first_m + (pid % (GRP * tiles_n)) % gsz;
-  const int tn = (pid % (GRP * tiles_n)) / gsz;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   v4i pre[CPT];
@@ -141,137 +259,148 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(const int8_t* __restrict__ CA,
     __syncthreads();
   }
 
-  // ---------------- epilogue ----------------
-  // lane (lr, lg), register r of tile (i, j):
-  //   n = n0 + wn*WN + i*32 + (r/4)*8 + lg*4 + r%4,  m = m0 + wm*WM + j*32 + lr
-  const int nb = n0 + wn * WN + lg * 4;
-  const int mb = m0 + wm * WM + lr;
+  fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * WM, n0 + wn * WN, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, idx,
+                               count, bias, out, c32);
+}
 
-  if (c32 != nullptr) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int m = mb + j * 32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = nb + i * 32 + q * 8;
-          int32_t* p = c32 + (int64_t)m * N + n;
-          if (OV && n + 3 < N) {
-            *reinterpret_cast<v4i*>(p) = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                             acc[i][j][4 * q + 3]};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < N) p[e] = acc[i][j][4 * q + e];
-          }
-        }
-      }
-  }
+// Large-tile forward kernel: 256 x 256 output tile, 4 waves of 128 x 128,
+// K stepped 128 bytes at a time through two swizzled LDS stages (64 KB each).
+// Global tiles come in through buffer loads (rows past M / N and columns past
+// K read as zero), are held in registers for one step and written to the
+// other stage; operand fragments are double-buffered in registers so that
+// LDS reads of the next 32-wide k slice overlap the MFMAs of the current one.
+// Requires K % 16 == 0.
+template <int DT, bool OV>
+__global__ __launch_bounds__(256, 1) void k_gemm_fwd_big(const int8_t* __restrict__ CA,
+                                                         const float* __restrict__ SCA, int M,
+                                                         const int8_t* __restrict__ CB,
+                                                         const float* __restrict__ SCB, int N, int K,
+                                                         const uint16_t* __restrict__ subA, int cap,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ count,
+                                                         const typename Elem<DT>::T* __restrict__ bias,
+                                                         typename Elem<DT>::T* __restrict__ out,
+                                                         int32_t* __restrict__ c32) {
+  constexpr int BM = 256, BN = 256, BK = 128, TI = 4, TJ = 4;
+  constexpr int STAGE = (BM + BN) * BK;        // bytes per LDS stage
+  constexpr int AOFF = BN * BK;                // A tile after the B tile
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
 
-  float sa[TJ];
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int m = mb + j * 32;
-    sa[j] = (m < M) ? SCA[m] : 0.0f;
-  }
-  v16f accf[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    float sb[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
-      sb[r] = (n < N) ? SCB[n] : 0.0f;
-    }
-    // (SCA * SCB) * fl32(1/127^2): exactly 1 when both scales are 127
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        accf[i][j][r] = (float)acc[i][j][r] * ((sa[j] * sb[r]) * (1.0f / 16129.0f));
-  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int wn = wave & 1, wm = wave >> 1;
 
-  // outlier columns: fp16 product accumulated into the same fp32 registers
-  int cnt = 0;
-  if (count != nullptr) {
-    cnt = *count;
-    if (cnt > cap) cnt = cap;
-  }
-  for (int jo = 0; jo < cnt; jo += 16) {
-    v8h P[TI], Q[TJ];
-    int kk[8];
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(CA + (int64_t)m0 * K, min(BM, M - m0) * K);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(CB + (int64_t)n0 * K, min(BN, N - n0) * K);
+
+  // global -> register slots: chunk c (16 bytes) of rows lrow + 32 i
+  const int lrow = tid >> 3, lc = tid & 7;
+  const int voff = lrow * K + 16 * lc;
+  const int woff = lrow * BK + 16 * (lc ^ lds_swz(lrow));
+  // fragment read offsets for the four 32-byte k slices of a stage
+  const int sw = lds_swz(lr);
+  int roff[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = jo + lg * 8 + e;
-      kk[e] = (j < cnt) ? idx[j] : -1;
+  for (int ks = 0; ks < 4; ++ks) roff[ks] = lr * BK + 16 * ((2 * ks + lg) ^ sw);
+  const int pb = wn * 128 * BK, qb = AOFF + wm * 128 * BK;
+
+  v4u R[16];
+  auto gload = [&](int kt) {
+    // chunks past K (contraction tail) must read as zero: push them out of range
+    const int keep = -(int)(kt + 16 * lc < K);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int oi = ((voff + kt + 32 * i * K) & keep) | (OOB_OFFSET & ~keep);
+      R[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rB, oi, 0, 0));
+      R[8 + i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rA, oi, 0, 0));
     }
+  };
+  auto swrite = [&](int st) {
+    int8_t* b = smem + st * STAGE + woff;
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int n = n0 + wn * WN + i * 32 + lr;
-      const bool nok = n < N;
-      const float sig = nok ? SCB[n] * (1.0f / 127.0f) : 0.0f;
-      const int8_t* wrow = CB + (int64_t)(nok ? n : 0) * K;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        P[i][e] = (nok && kk[e] >= 0) ? (_Float16)((float)wrow[kk[e]] * sig) : (_Float16)0.0f;
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<v4u*>(b + i * 32 * BK) = R[i];
+      *reinterpret_cast<v4u*>(b + AOFF + i * 32 * BK) = R[8 + i];
     }
+  };
+
+  v16i acc[TI][TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int m = m0 + wm * WM + j * 32 + lr;
-      const bool mok = m < M;
-      const uint16_t* srow = subA + (int64_t)(mok ? m : 0) * cap;
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int jj = jo + lg * 8 + e;
-        Q[j][e] = (mok && jj < cnt) ? __builtin_bit_cast(_Float16, srow[jj]) : (_Float16)0.0f;
-      }
-    }
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
+
+  v4i F[2][8];
+  auto fread = [&](int st, int ks, int b) {
+    const int8_t* base = smem + st * STAGE + roff[ks];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) F[b][i] = *reinterpret_cast<const v4i*>(base + pb + i * 32 * BK);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) F[b][4 + j] = *reinterpret_cast<const v4i*>(base + qb + j * 32 * BK);
+  };
+  auto mma = [&](int b) {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P[i], Q[j], accf[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[b][i], F[b][4 + j], acc[i][j], 0, 0, 0);
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  swrite(0);
+  __syncthreads();
+  fread(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    gload((kt + 1) * BK);          // past the end: all offsets out of range, zeros
+    fread(st, 1, 1);
+    mma(0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_DS_R, 1);
+      I8L_SGB(SG_VMEM_R, 2);
+    }
+    I8L_SGB(SG_MFMA, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    fread(st, 2, 0);
+    mma(1);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_DS_R, 1);
+    }
+    I8L_SGB(SG_MFMA, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    fread(st, 3, 1);
+    mma(0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_DS_R, 1);
+    }
+    I8L_SGB(SG_MFMA, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    swrite(st ^ 1);
+    mma(1);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_DS_W, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    fread(st ^ 1, 0, 0);
   }
 
-  // bias, cast, store
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    float bv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
-      bv[r] = (bias != nullptr && n < N) ? Elem<DT>::to_f32(bias[n]) : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int m = mb + j * 32;
-      if (m >= M) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nb + i * 32 + q * 8;
-        T* p = out + (int64_t)m * N + n;
-        T v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = Elem<DT>::from_f32(accf[i][j][4 * q + e] + bv[4 * q + e]);
-        if (OV && n + 3 < N) {
-          if constexpr (DT == DT_F32) {
-            *reinterpret_cast<v4f*>(p) = v4f{v[0], v[1], v[2], v[3]};
-          } else {
-            v2u w;
-            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
-            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
-            *reinterpret_cast<v2u*>(p) = w;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) p[e] = v[e];
-        }
-      }
-    }
-  }
+  fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 128, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, idx,
+                               count, bias, out, c32);
 }
 
 template <int BM, int BN, int BK, int DT, bool KV, bool OV>
@@ -294,14 +423,34 @@ static hipError_t launch_fwd_cfg(const int8_t* CA, const float* SCA, int M, cons
   return hipGetLastError();
 }
 
+template <int DT, bool OV>
+static hipError_t launch_fwd_big(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
+                                 int N, int K, const uint16_t* subA, int cap, const int32_t* idx,
+                                 const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
+  typedef typename Elem<DT>::T T;
+  constexpr size_t lds = (size_t)2 * (256 + 256) * 128;
+  auto kern = k_gemm_fwd_big<DT, OV>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count,
+                     static_cast<const T*>(bias), static_cast<T*>(out), c32);
+  return hipGetLastError();
+}
+
 template <int DT, bool KV, bool OV>
 static hipError_t launch_fwd_dt(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
                                 int N, int K, const uint16_t* subA, int cap, const int32_t* idx, const int32_t* count,
                                 const void* bias, void* out, int32_t* c32, hipStream_t st) {
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 200)
-    return launch_fwd_cfg<256, 256, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out,
-                                                    c32, st);
+  if constexpr (KV) {
+    if (big_tiles >= 64)
+      return launch_fwd_big<DT, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st);
+  }
   return launch_fwd_cfg<128, 128, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32,
                                                   st);
 }

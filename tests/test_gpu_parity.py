@@ -171,6 +171,36 @@ def test_backward_parity(I8, dt, M, K, N):
     assert_float_gate(host(gb), dt, gb64, "grad_bias", tight_rel=2.0 ** -16)
 
 
+# shapes with at least 64 output tiles of 256 x 256, which select the
+# large-tile pipelined kernels; ragged in every dimension (partial tiles and a
+# contraction tail that is not a multiple of the k step)
+BIG_FWD = [(2100, 1040, 2090), (2048, 4096, 2048), (1030, 528, 4100), (2304, 16, 2304)]
+BIG_BWD = [(2100, 2088, 1044), (2048, 2048, 2048), (2060, 1000, 4100), (2304, 8, 2304)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("M,K,N", BIG_FWD)
+def test_forward_parity_large_tiles(I8, dt, M, K, N):
+    A, W, b, _ = _layer(dt, M, K, N, 7, n_out=5)
+    CB, SCB, cb, scb = _check_weights(I8, W)
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1, 255, 256, 257]]))
+    _forward_and_check(I8, A, dt, CB, SCB, cb, scb, b, 6.0, rows=rows)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("M,N,K", BIG_BWD)
+def test_backward_parity_large_tiles(I8, dt, M, N, K):
+    _, W, _, G = _layer(dt, M, K, N, 8)
+    CB, SCB, cb, scb = _check_weights(I8, W)
+    gA, gb = I8.int8_linear_backward_input(dev(G, dt), CB, SCB, with_grad_bias=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1, 255, 256, 257]]))
+    r = oracle.linear_backward_input(G, dt, cb, scb, rows=rows)
+    assert_float_gate(host(gA)[rows], dt, r["y"], "grad_A")
+    gb64, _ = oracle.grad_bias(G, dt)
+    assert_float_gate(host(gb), dt, gb64, "grad_bias", tight_rel=2.0 ** -16)
+
+
 @pytest.mark.parametrize("dt", DTS)
 def test_forward_zero_input_is_bias_bitwise(I8, dt):
     M, K, N = 70, 96, 130

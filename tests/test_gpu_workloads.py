@@ -47,6 +47,7 @@ def test_workload_layer(I8, name, li):
     assert_bits_equal(host(CB), cb, "CB")
     assert_bits_equal(host(SCB), scb, "SCB")
     del W
+    print("  weights bit-exact", flush=True)
     A = workloads.make_activation(wl, li)
     b = workloads.make_bias(wl, li)
     M, K, N = L.M, L.K, L.N
@@ -56,6 +57,7 @@ def test_workload_layer(I8, name, li):
                                  workspace=ws)
     torch.cuda.synchronize()
     rows = _rows(M)
+    print("  forward done on GPU; oracle ...", flush=True)
     f = oracle.linear_forward(A, dt, cb, scb, b, tau, rows=rows)
     q = f["q"]
     lay = I8.forward_layout(M, K, K)
@@ -72,6 +74,7 @@ def test_workload_layer(I8, name, li):
     assert_bits_equal(host(c32.index_select(0, rt)), f["c32"].astype(np.int32), "C32 (sampled rows)")
     assert_float_gate(host(out.index_select(0, rt)), dt, f["y"], "out (sampled rows)")
     del A, c32, out, ws, f, q
+    print(f"  forward parity ok (|O|={cnt})", flush=True)
     G = workloads.make_grad(wl, li)
     gA, gb = I8.int8_linear_backward_input(dev(G, dt), CB, SCB, with_grad_bias=b is not None)
     torch.cuda.synchronize()

@@ -18,6 +18,18 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Two bf16 values packed in a word -> two fp16 values packed in a word (RNE).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const v2f f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h));
+}
+// Two fp32 values -> two fp16 values packed in a word (RNE).
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
+  const v2f f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h));
+}
 
 enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 

@@ -62,6 +62,8 @@ enum {
 /* Largest contraction length whose int32 accumulator cannot overflow:
  * 127 * 127 * K < 2^31. */
 #define I8L_MAX_K 133144
+/* Widest row int8_quantize_rowwise accepts (column flags kept on chip). */
+#define I8L_MAX_COLS 262144
 
 /* Short text for an error code (static storage). */
 const char* int8_linear_strerror(int code);
@@ -81,6 +83,7 @@ const char* int8_linear_strerror(int code);
  * outlier_count 1 int32 (= |O|, may exceed cap: overflow is then visible);
  * sub rows x cap fp16 bits (leading dimension cap; only columns j < |O| are
  * written). outlier_idx / sub may be NULL when cap = 0.
+ * cols <= I8L_MAX_COLS, else I8L_ESHAPE.
  * Weights are quantized with this call and tau off: CB = codes, SCB = s.
  * ------------------------------------------------------------------------ */
 size_t int8_quantize_rowwise_workspace_bytes(int64_t rows, int64_t cols);

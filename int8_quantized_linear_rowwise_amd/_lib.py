@@ -14,6 +14,7 @@ LIB_PATH = os.environ.get("I8L_LIBRARY", os.path.join(_HERE, "libint8lin.so"))
 I8L_F32, I8L_F16, I8L_BF16 = 0, 1, 2
 I8L_OK, I8L_EINVAL, I8L_EDTYPE, I8L_ESHAPE, I8L_EWORKSPACE, I8L_EHIP, I8L_EOVERFLOW = 0, -1, -2, -3, -4, -5, -6
 I8L_MAX_K = 133144
+I8L_MAX_COLS = 262144
 
 # every symbol the header declares, with (restype, argtypes)
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t

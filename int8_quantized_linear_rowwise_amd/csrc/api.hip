@@ -15,13 +15,8 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool valid_dtype(int dt) { return dt == I8L_F32 || dt == I8L_F16 || dt == I8L_BF16; }
 
-size_t mask_words(int64_t cols) { return (size_t)((cols + 31) / 32); }
-
-// quantizer scratch: bitmask + per-word prefix
-size_t quant_scratch_bytes(int64_t cols) {
-  const size_t nw = mask_words(cols) > 0 ? mask_words(cols) : 1;
-  return align_up(nw * 4) * 2;
-}
+// quantizer scratch: per-slab column bits, column bitmask, per-word prefix
+size_t quant_scratch_bytes(int64_t rows, int64_t cols) { return align_up(i8l::quant_scratch_words(rows, cols) * 4); }
 
 bool fwd_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* L) {
   if (M < 0 || K < 0 || cap < 0) return false;
@@ -37,7 +32,7 @@ bool fwd_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* L) {
   L->sub = off;
   off += align_up((size_t)M * (size_t)cap * 2 > 0 ? (size_t)M * (size_t)cap * 2 : 2);
   // quantizer scratch after the layout proper
-  off += quant_scratch_bytes(K);
+  off += quant_scratch_bytes(M, K);
   L->total = off;
   return true;
 }
@@ -62,9 +57,8 @@ const char* int8_linear_strerror(int code) {
 }
 
 size_t int8_quantize_rowwise_workspace_bytes(int64_t rows, int64_t cols) {
-  (void)rows;
-  if (cols < 0) return 0;
-  return quant_scratch_bytes(cols);
+  if (rows < 0 || cols < 0) return 0;
+  return quant_scratch_bytes(rows, cols);
 }
 
 int int8_quantize_rowwise(const void* X, int dtype, int64_t rows, int64_t cols, float threshold, int8_t* codes,
@@ -72,17 +66,15 @@ int int8_quantize_rowwise(const void* X, int dtype, int64_t rows, int64_t cols, 
                           int32_t cap, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dtype)) return I8L_EDTYPE;
   if (rows < 0 || cols < 0 || cap < 0) return I8L_EINVAL;
-  if (rows > INT32_MAX || cols > INT32_MAX || rows * cols > ((int64_t)1 << 40)) return I8L_ESHAPE;
+  if (rows > INT32_MAX || cols > I8L_MAX_COLS || rows * cols > ((int64_t)1 << 40)) return I8L_ESHAPE;
   if (outlier_count == nullptr) return I8L_EINVAL;
   if (rows > 0 && (row_scale == nullptr || (cols > 0 && (X == nullptr || codes == nullptr)))) return I8L_EINVAL;
   if (cap > 0 && (outlier_idx == nullptr || (rows > 0 && sub == nullptr))) return I8L_EINVAL;
-  const size_t need = quant_scratch_bytes(cols);
+  const size_t need = quant_scratch_bytes(rows, cols);
   if (ws == nullptr || ws_bytes < need) return I8L_EWORKSPACE;
   if ((uintptr_t)ws % ALIGN) return I8L_EINVAL;
-  uint32_t* mask = static_cast<uint32_t*>(ws);
-  int32_t* prefix = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
   return hip_status(i8l::launch_quantize(dtype, X, rows, (int)cols, threshold, codes, row_scale, outlier_idx,
-                                         outlier_count, sub, cap, mask, prefix, (hipStream_t)stream));
+                                         outlier_count, sub, cap, static_cast<uint32_t*>(ws), (hipStream_t)stream));
 }
 
 size_t int8_linear_forward_workspace_bytes(int64_t M, int64_t K, int32_t cap) {
@@ -120,12 +112,9 @@ int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const in
   float* SCA = reinterpret_cast<float*>(w + L.scale);
   int8_t* CA = reinterpret_cast<int8_t*>(w + L.codes);
   uint16_t* subA = reinterpret_cast<uint16_t*>(w + L.sub);
-  const size_t qs = quant_scratch_bytes(K);
-  uint32_t* mask = reinterpret_cast<uint32_t*>(w + L.total - qs);
-  int32_t* prefix = reinterpret_cast<int32_t*>(w + L.total - qs / 2);
+  uint32_t* qscratch = reinterpret_cast<uint32_t*>(w + L.total - quant_scratch_bytes(M, K));
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = i8l::launch_quantize(dtype, A, M, (int)K, threshold, CA, SCA, idx, count, subA, cap, mask,
-                                      prefix, st);
+  hipError_t e = i8l::launch_quantize(dtype, A, M, (int)K, threshold, CA, SCA, idx, count, subA, cap, qscratch, st);
   if (e != hipSuccess) return I8L_EHIP;
   e = i8l::launch_gemm_fwd(dtype, CA, SCA, (int)M, CB, SCB, (int)N, (int)K, subA, cap, idx, count, bias, out, c32,
                            st);

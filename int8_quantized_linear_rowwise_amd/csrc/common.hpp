@@ -129,12 +129,21 @@ enum : int { SG_MFMA = 0x008, SG_VMEM_R = 0x020, SG_DS_R = 0x100, SG_DS_W = 0x20
 // XCD's L2), and within a run tiles go down groups of 8 row-tiles before
 // moving to the next column-tile, so concurrently running workgroups share
 // operand tiles.
+#ifndef I8L_TILE_GRP
+#define I8L_TILE_GRP 4
+#endif
+#ifndef I8L_TILE_XCD
+#define I8L_TILE_XCD 1
+#endif
 __device__ __forceinline__ void tile_coords(int bid, int tiles_r, int tiles_c, int& tr, int& tc) {
   const int nt = tiles_r * tiles_c;
-  const int x = bid & 7, i = bid >> 3;
-  const int base = nt >> 3, rem = nt & 7;
-  const int pid = x * base + (x < rem ? x : rem) + i;
-  constexpr int GRP = 8;
+  int pid = bid;
+  if (I8L_TILE_XCD) {
+    const int x = bid & 7, i = bid >> 3;
+    const int base = nt >> 3, rem = nt & 7;
+    pid = x * base + (x < rem ? x : rem) + i;
+  }
+  constexpr int GRP = I8L_TILE_GRP;
   const int group = pid / (GRP * tiles_c);
   const int first = group * GRP;
   const int gsz = min(tiles_r - first, GRP);

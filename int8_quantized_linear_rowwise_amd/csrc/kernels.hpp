@@ -7,11 +7,12 @@
 namespace i8l {
 
 // Quantizer: X (rows x cols, dtype dt) -> codes, scale, outlier list (first
-// `cap` entries), count, sub (rows x cap fp16). mask / prefix: ceil(cols/32)
-// words each of scratch.
+// `cap` entries), count, sub (rows x cap fp16). scratch: quant_scratch_words()
+// 32-bit words.
+size_t quant_scratch_words(int64_t rows, int64_t cols);
 hipError_t launch_quantize(int dt, const void* X, int64_t rows, int cols, float tau, int8_t* codes, float* scale,
-                           int32_t* idx, int32_t* count, uint16_t* sub, int cap, uint32_t* mask,
-                           int32_t* prefix, hipStream_t st);
+                           int32_t* idx, int32_t* count, uint16_t* sub, int cap, uint32_t* scratch,
+                           hipStream_t st);
 
 // Forward GEMM with fused epilogue: out = D(CA.CB^T * SCA SCB / 127^2
 // + subA . Wdq[:, idx]^T + bias); optional int32 export of CA.CB^T.

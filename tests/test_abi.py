@@ -84,6 +84,7 @@ def test_quantize_host_errors(L):
     assert call(wsb=ws - 1) == L.I8L_EWORKSPACE
     assert call(ws=FAKE + 8) == L.I8L_EINVAL
     assert call(R=1 << 33) == L.I8L_ESHAPE
+    assert call(C=L.I8L_MAX_COLS + 1, wsb=1 << 30) == L.I8L_ESHAPE
 
 
 def test_forward_host_errors(L):

@@ -151,6 +151,48 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_r, int tiles_c, i
   tc = (pid % (GRP * tiles_c)) / gsz;
 }
 
+// Output tiles of 256 x 256 16-bit values are staged in LDS (512 bytes per
+// row) so that global stores cover whole rows: lanes holding four
+// consecutive columns of 32 different rows write 8 bytes each into LDS, then
+// each half-wave stores one 512-byte row. The 16-byte chunk c of row r sits at
+// chunk position c ^ (r & 31), which spreads the 32 rows of one LDS write
+// over all banks.
+__device__ __forceinline__ int otile_off(int row, int chunk) { return row * 512 + 16 * (chunk ^ (row & 31)); }
+
+// Store rows [32 w, 32 w + 32) of an LDS output tile (wave w of eight) to
+// dst[(r0 + row) * ld + c0 + col], clipped to R rows and C columns.
+template <typename T>
+__device__ __forceinline__ void otile_store(const char* ot, T* __restrict__ dst, int64_t ld, int r0, int c0, int R,
+                                            int C, int wave, int lane) {
+  static_assert(sizeof(T) == 2, "16-bit outputs");
+  const int ch = lane & 31;
+  const int c = c0 + ch * 8;
+  const bool vec = (ld % 8 == 0) && ((uintptr_t)dst % 16 == 0);
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int row = 32 * wave + 2 * it + (lane >> 5);
+    const int r = r0 + row;
+    if (r >= R) continue;
+    const v4u v = *reinterpret_cast<const v4u*>(ot + otile_off(row, ch));
+    T* p = dst + (int64_t)r * ld + c;
+    if (c + 8 <= C) {
+      if (vec) {
+        *reinterpret_cast<v4u*>(p) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[2 * e] = __builtin_bit_cast(T, (uint16_t)(v[e] & 0xffffu));
+          p[2 * e + 1] = __builtin_bit_cast(T, (uint16_t)(v[e] >> 16));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c + e < C) p[e] = __builtin_bit_cast(T, (uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+    }
+  }
+}
+
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -670,34 +670,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_w8(const typename Elem<DT>:
 
   // lane (lr, lg), register r of tile (i, j):
   //   k = k0 + wk*128 + i*32 + (r/4)*8 + lg*4 + r%4,  m = m0 + wm*64 + j*32 + lr
+  // The tile goes through LDS (row m, 16-byte chunk of 8 k) and leaves as
+  // whole rows.
   typedef typename Elem<DT>::T T;
-  const int kb = k0 + wk * 128 + lg * 4;
+  __syncthreads();   // every wave is done with the operand stages
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
-    const int m = m0 + wm * 64 + j * 32 + lr;
-    if (m >= M) continue;
+    const int row = wm * 64 + j * 32 + lr;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int k = kb + i * 32 + q * 8;
-        T* p = gA + (int64_t)m * K + k;
-        T v[4];
+        v2u w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = Elem<DT>::from_f32(acc[i][j][4 * q + e]);
-        if (OV && k + 3 < K) {
-          v2u w;
-          w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
-          w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
-          *reinterpret_cast<v2u*>(p) = w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (k + e < K) p[e] = v[e];
-        }
+        for (int e = 0; e < 2; ++e)
+          w[e] = (uint32_t)__builtin_bit_cast(uint16_t, Elem<DT>::from_f32(acc[i][j][4 * q + 2 * e])) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, Elem<DT>::from_f32(acc[i][j][4 * q + 2 * e + 1])) << 16);
+        *reinterpret_cast<v2u*>(bsm + otile_off(row, wk * 16 + i * 4 + q) + 8 * lg) = w;
       }
     }
   }
+  __syncthreads();
+  otile_store<T>(bsm, gA, K, m0, k0, M, K, wave, lane);
 }
 
 template <int DT, bool OV>

@@ -29,14 +29,22 @@ namespace i8l {
 // Fused epilogue shared by the forward kernels. A wave owns TI x TJ tiles of
 // 32 x 32 (n x m); lane (lr, lg) holds, for tile (i, j) and register r,
 //   n = nw + i*32 + (r/4)*8 + lg*4 + r%4,   m = mw + j*32 + lr.
-template <int TI, int TJ, int DT, bool OV>
+//
+// With LDS_OUT (16-bit outputs, eight waves over a 256 x 256 block tile whose
+// origin is (tm0, tn0)), the results are written to the LDS tile `ot` (row m,
+// 16-byte chunk of 8 features) instead of global memory; the caller then
+// stores whole rows with otile_store. The call starts with a block barrier.
+template <int TI, int TJ, int DT, bool OV, bool LDS_OUT = false>
 __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw, int lr, int lg, int M, int N, int K,
                                              const float* __restrict__ SCA, const int8_t* __restrict__ CB,
                                              const float* __restrict__ SCB, const uint16_t* __restrict__ subA,
                                              int cap, const int32_t* __restrict__ idx,
                                              const int32_t* __restrict__ count,
                                              const typename Elem<DT>::T* __restrict__ bias,
-                                             typename Elem<DT>::T* __restrict__ out, int32_t* __restrict__ c32) {
+                                             typename Elem<DT>::T* __restrict__ out, int32_t* __restrict__ c32,
+                                             char* ot = nullptr, int tm0 = 0, int tn0 = 0) {
+  static_assert(!LDS_OUT || DT != DT_F32, "LDS output staging holds 16-bit values");
+  if constexpr (LDS_OUT) __syncthreads();   // the operand stages are no longer read
   typedef typename Elem<DT>::T T;
   const int nb = nw + lg * 4;
   const int mb = mw + lr;
@@ -126,6 +134,25 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
     for (int r = 0; r < 16; ++r) {
       const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
       bv[r] = (bias != nullptr && n < N) ? Elem<DT>::to_f32(bias[n]) : 0.0f;
+    }
+    if constexpr (LDS_OUT) {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int row = mb + j * 32 - tm0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int chunk = (nw - tn0 + i * 32 + q * 8) >> 3;
+          v2u w;
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            w[e] = (uint32_t)__builtin_bit_cast(uint16_t, Elem<DT>::from_f32(accf[j][4 * q + 2 * e] + bv[4 * q + 2 * e])) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t,
+                                                 Elem<DT>::from_f32(accf[j][4 * q + 2 * e + 1] + bv[4 * q + 2 * e + 1]))
+                    << 16);
+          *reinterpret_cast<v2u*>(ot + otile_off(row, chunk) + 8 * lg) = w;
+        }
+      }
+      continue;
     }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
@@ -552,8 +579,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
     fread(st ^ 1, 0, 0);
   }
 
-  fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 64, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, idx,
-                               count, bias, out, c32);
+  if constexpr (DT == DT_F32) {
+    fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 64, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, idx,
+                                 count, bias, out, c32);
+  } else {
+    // output tile through LDS, stored as whole rows
+    char* ot = reinterpret_cast<char*>(smem);
+    fwd_epilogue<TI, TJ, DT, OV, true>(acc, m0 + wm * 64, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap,
+                                       idx, count, bias, out, c32, ot, m0, n0);
+    __syncthreads();
+    otile_store<typename Elem<DT>::T>(ot, out, N, m0, n0, M, N, wave, lane);
+  }
 }
 
 template <int DT, bool OV>

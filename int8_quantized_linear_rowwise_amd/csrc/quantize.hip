@@ -6,76 +6,46 @@
 // exceeds the threshold leave the int8 path ("4. Mixed-precision
 // decomposition matmul") and are kept as a dense fp16 sub-matrix.
 //
-// Three kernels on the caller's stream (HBM-bound; the second read of X is
+// Two kernels on the caller's stream (HBM-bound; the second read of X is
 // usually served by the Infinity Cache):
-//   k_outlier_flags    one read of X. A workgroup covers a slab of rows and
-//                      512 columns; per column it keeps the largest magnitude
-//                      in the storage format's own bits (magnitude bits order
-//                      like the values, and the fp16 cast is monotone), then
-//                      casts once and compares with tau. Each workgroup writes
-//                      its own words of a [slab][column-word] bit array, so
-//                      nothing needs clearing beforehand.
-//   k_outlier_compact  one workgroup: OR over slabs (in LDS), per-word
-//                      exclusive popcount prefix, ascending outlier list,
-//                      count (an OR and a prefix scan: order-independent).
-//   k_rowquant         second read of X, one wave per row: absmax over
-//                      non-outlier columns (again on magnitude bits), s as an
-//                      fp16 value, inv = 127 / s (IEEE division), codes =
-//                      clamp(rint(x * inv), +-127), 0 on outlier columns,
-//                      outlier values copied into the dense fp16 sub-matrix.
+//   k_colflags   one read of X. A workgroup covers 64 columns of a slab of
+//                rows (at most 16 slabs); per column it keeps the largest
+//                magnitude in the storage format's own bits (magnitude bits
+//                order like the values, and the fp16 cast is monotone), then
+//                casts once and compares with tau. Each workgroup writes its
+//                own two words of a [slab][column-word] bit array, so nothing
+//                needs clearing beforehand.
+//   k_rowquant   second read of X. Every workgroup first ORs the slab words
+//                into the column mask and computes the per-word popcount
+//                prefix in LDS (a few KB from L2); workgroup 0 also writes the
+//                ascending outlier list and the count. Then one wave per row:
+//                absmax over non-outlier columns (on magnitude bits), s as an
+//                fp16 value, inv = 127 / s (IEEE division), codes =
+//                rint(fl32(x * inv)) (|code| <= 127 by construction), 0 on
+//                outlier columns, outlier values copied into the dense fp16
+//                sub-matrix.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace i8l {
 
-constexpr int FLAG_COLS = 512;     // columns per flags workgroup (64 lanes x 8)
-constexpr int FLAG_SLABS = 256;    // at most this many row slabs in the flags pass
-constexpr int FLAG_MAX_WORDS = 8192;  // column words the compaction keeps in LDS (K <= 262144)
+constexpr int CF_COLS = 64;          // columns per flags workgroup (8 lanes x 8 columns)
+constexpr int CF_MAX_SLABS = 16;     // row slabs of the flags pass
+constexpr int CF_SLAB_WORDS = 2048;  // slabs * words the row kernel ORs per workgroup (at most)
+constexpr int RQ_MAX_BLOCKS = 1024;  // row-kernel workgroups (four rows at a time each)
 
-// ---------------------------------------------------------------------------
-// magnitude bits of 8 consecutive elements (storage format)
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
-template <int DT> struct Mag8;
-
-template <> struct Mag8<DT_F32> {
-  uint32_t m[8];
-  __device__ void reset() {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m[e] = 0u;
-  }
-  __device__ void add(const v4u& a, const v4u& b) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      m[e] = max(m[e], a[e] & 0x7fffffffu);
-      m[e + 4] = max(m[e + 4], b[e] & 0x7fffffffu);
-    }
-  }
-  __device__ float half_mag(int e) const { return (float)(_Float16)__uint_as_float(m[e]); }
-};
-
-template <int DT> struct Mag8h {
-  uint32_t m[4];  // two 16-bit magnitudes per word
-  __device__ void reset() {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m[e] = 0u;
-  }
-  __device__ void add(const v4u& a) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w = a[e] & 0x7fff7fffu;
-      const uint32_t lo = max(m[e] & 0xffffu, w & 0xffffu);
-      const uint32_t hi = max(m[e] >> 16, w >> 16);
-      m[e] = lo | (hi << 16);
-    }
-  }
-  __device__ float half_mag(int e) const {
-    const uint16_t b = (uint16_t)((e & 1) ? (m[e >> 1] >> 16) : (m[e >> 1] & 0xffffu));
-    if constexpr (DT == DT_F16) return (float)__builtin_bit_cast(_Float16, b);
-    else return (float)(_Float16)bf16_to_f32(b);
-  }
-};
-template <> struct Mag8<DT_F16> : Mag8h<DT_F16> {};
-template <> struct Mag8<DT_BF16> : Mag8h<DT_BF16> {};
+// Slabs of the flags pass for a matrix: enough workgroups to fill the chip,
+// few enough words for every row-kernel workgroup to OR them.
+static int colflag_slabs(int64_t rows, int64_t cols) {
+  const int64_t nw = (cols + 31) / 32;
+  int64_t s = CF_SLAB_WORDS / (nw > 0 ? nw : 1);
+  if (s > CF_MAX_SLABS) s = CF_MAX_SLABS;
+  if (s < 1) s = 1;
+  if (s > rows) s = rows > 0 ? rows : 1;
+  return (int)s;
+}
 
 // Load 8 consecutive elements of row r (cols c0..c0+7) as raw words, zero
 // past the end of the row. vec: rows are 16-byte aligned and cols % 8 == 0.
@@ -102,135 +72,6 @@ __device__ __forceinline__ void load_raw8(const typename Elem<DT>::T* __restrict
   }
   a = v4u{w[0], w[1], w[2], w[3]};
   if constexpr (DT == DT_F32) b = v4u{w[4], w[5], w[6], w[7]};
-}
-
-// grid: x over column groups of 512, y over row slabs. Four waves split the
-// slab's rows (wave w takes rows r0 + w, r0 + w + 4, ...); their flags are
-// OR-ed in LDS and the workgroup writes its 16 words of bits[slab][word].
-template <int DT>
-__global__ __launch_bounds__(256) void k_outlier_flags(const typename Elem<DT>::T* __restrict__ X, int64_t rows,
-                                                       int cols, float tau, int64_t rows_per_slab, int vec,
-                                                       int nwords, uint32_t* __restrict__ bits) {
-  typedef typename Elem<DT>::T T;
-  __shared__ uint32_t sw[4][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c0 = blockIdx.x * FLAG_COLS + lane * 8;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_slab;
-  int64_t r1 = r0 + rows_per_slab;
-  if (r1 > rows) r1 = rows;
-  Mag8<DT> acc;
-  acc.reset();
-  if (c0 < cols) {
-    int64_t r = r0 + wave;
-    const T* p = X + r * (int64_t)cols;
-    const int64_t step = 4 * (int64_t)cols;
-    for (; r + 28 < r1; r += 32, p += 8 * step) {
-      v4u a[8], b[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) load_raw8<DT>(p + u * step, c0, cols, vec, a[u], b[u]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if constexpr (DT == DT_F32) acc.add(a[u], b[u]);
-        else acc.add(a[u]);
-      }
-    }
-    for (; r < r1; r += 4, p += step) {
-      v4u a, b;
-      load_raw8<DT>(p, c0, cols, vec, a, b);
-      if constexpr (DT == DT_F32) acc.add(a, b);
-      else acc.add(a);
-    }
-  }
-  uint32_t byte = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (c0 + e < cols && acc.half_mag(e) > tau) byte |= 1u << e;
-  // four lanes form one 32-bit word (columns 32w .. 32w+31)
-  uint32_t word = byte << (8 * (lane & 3));
-  word |= __shfl_xor(word, 1, 64);
-  word |= __shfl_xor(word, 2, 64);
-  if ((lane & 3) == 0) sw[wave][lane >> 2] = word;
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    const int w = blockIdx.x * (FLAG_COLS / 32) + threadIdx.x;
-    if (w < nwords)
-      bits[(int64_t)blockIdx.y * nwords + w] =
-          sw[0][threadIdx.x] | sw[1][threadIdx.x] | sw[2][threadIdx.x] | sw[3][threadIdx.x];
-  }
-}
-
-// One workgroup of 1024 threads: mask = OR over slabs; prefix; list; count.
-// nwords <= FLAG_MAX_WORDS (checked on the host).
-__global__ __launch_bounds__(1024) void k_outlier_compact(const uint32_t* __restrict__ bits, int slabs,
-                                                          int nwords, uint32_t* __restrict__ mask,
-                                                          int32_t* __restrict__ prefix, int32_t* __restrict__ idx,
-                                                          int cap, int32_t* __restrict__ count) {
-  __shared__ int wsum[16];
-  __shared__ uint32_t smask[FLAG_MAX_WORDS];
-  const int t = threadIdx.x;
-  for (int w = t; w < nwords; w += 1024) smask[w] = 0u;
-  __syncthreads();
-  // parallel OR: thread t takes word t % nwords of slabs t / nwords + k * stride,
-  // eight independent loads at a time, then one LDS OR per word and thread
-  if (nwords > 0) {
-    const int lanes_per_word = max(1, 1024 / nwords);
-    const int w = t % nwords, s0 = t / nwords;
-    if (t < lanes_per_word * nwords) {
-      uint32_t m = 0u;
-      int s = s0;
-      for (; s + 7 * lanes_per_word < slabs; s += 8 * lanes_per_word) {
-        uint32_t v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = bits[(int64_t)(s + u * lanes_per_word) * nwords + w];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) m |= v[u];
-      }
-      for (; s < slabs; s += lanes_per_word) m |= bits[(int64_t)s * nwords + w];
-      if (m) atomicOr(&smask[w], m);
-      // words beyond the first 1024 (nwords > 1024)
-      for (int w2 = t + 1024; w2 < nwords; w2 += 1024) {
-        uint32_t m2 = 0u;
-        for (int s2 = 0; s2 < slabs; ++s2) m2 |= bits[(int64_t)s2 * nwords + w2];
-        if (m2) atomicOr(&smask[w2], m2);
-      }
-    }
-  }
-  __syncthreads();
-  for (int w = t; w < nwords; w += 1024) mask[w] = smask[w];
-  const int per = (nwords + 1023) / 1024;
-  const int w0 = t * per;
-  int local = 0;
-  for (int i = 0; i < per; ++i)
-    if (w0 + i < nwords) local += __popc(smask[w0 + i]);
-  const int lane = t & 63, wid = t >> 6;
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
-  if (lane == 63) wsum[wid] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int i = 0; i < wid; ++i) base += wsum[i];
-  int run = base + incl - local;
-  for (int i = 0; i < per; ++i) {
-    const int w = w0 + i;
-    if (w >= nwords) break;
-    uint32_t m = smask[w];
-    prefix[w] = run;
-    while (m) {
-      const int b = __ffs(m) - 1;
-      if (run < cap) idx[run] = w * 32 + b;
-      ++run;
-      m &= m - 1;
-    }
-  }
-  if (t == 1023) {
-    int total_count = 0;
-    for (int i = 0; i < 16; ++i) total_count += wsum[i];
-    *count = total_count;
-  }
 }
 
 // fp16 value (as fp32) of element e of a raw 8-element chunk
@@ -261,57 +102,143 @@ __device__ __forceinline__ float mag_to_half_value(uint32_t m) {
   else return (float)(_Float16)bf16_to_f32((uint16_t)m);
 }
 
-// Row quantization: one wave per row; a wave walks rows row0, row0 + W, ...
-// (W waves in the grid). Rows of at most 64 * NCH chunks of 8 elements stay in
-// registers, and the next row's loads are issued before the current row is
-// quantized (two register buffers); wider rows stream twice through the
-// cache, one row at a time. The column bitmask is staged in LDS.
-// Outlier values of one 8-column chunk into the dense fp16 sub-matrix (rare:
-// kept out of line so that it adds no registers to the main path).
+// ---------------------------------------------------------------------------
+// column flags: grid (ceil(cols / 64), slabs), 256 threads. Lane l reads the
+// 8-column chunk l & 7 of rows r0 + 8 * wave + (l >> 3) + 32 i; the running
+// maximum is kept on magnitude bits (two 16-bit magnitudes per word for fp16
+// and bf16). Lanes and waves sharing a chunk are then combined, the maxima
+// cast to fp16 once and compared with tau, and the workgroup writes words
+// 2 bx and 2 bx + 1 of bits[slab].
 template <int DT>
-__device__ __noinline__ void put_outliers(uint16_t* __restrict__ srow, const uint32_t* __restrict__ smask,
-                                          const int32_t* __restrict__ prefix, int c0, uint32_t om, v4u a, v4u b,
-                                          int cap) {
-  const int w = c0 >> 5;
-  const uint32_t mw = smask[w];
-  const int base = prefix[w];
-  for (int e = 0; e < 8; ++e) {
-    if ((om >> e) & 1u) {
-      const int c = c0 + e;
-      const int j = base + __popc(mw & ((1u << (c & 31)) - 1u));
-      if (j < cap) srow[j] = __builtin_bit_cast(uint16_t, (_Float16)chunk_val<DT>(a, b, e));
+__global__ __launch_bounds__(256) void k_colflags(const typename Elem<DT>::T* __restrict__ X, int64_t rows,
+                                                  int cols, float tau, int64_t rows_per_slab, int vec, int nwords,
+                                                  uint32_t* __restrict__ bits) {
+  typedef typename Elem<DT>::T T;
+  constexpr int NW = (DT == DT_F32) ? 8 : 4;   // words of magnitudes per 8-column chunk
+  __shared__ uint32_t sm[4][8][NW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cc = lane & 7, ro = lane >> 3;
+  const int c0 = blockIdx.x * CF_COLS + cc * 8;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_slab;
+  const int64_t r1 = min(rows, r0 + rows_per_slab);
+
+  uint32_t m[NW];
+#pragma unroll
+  for (int d = 0; d < NW; ++d) m[d] = 0u;
+  auto add = [&](const v4u& a, const v4u& b) {
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        m[d] = max(m[d], a[d] & 0x7fffffffu);
+        m[d + 4] = max(m[d + 4], b[d] & 0x7fffffffu);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        m[d] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, m[d]),
+                                                                      __builtin_bit_cast(us2, a[d] & 0x7fff7fffu)));
     }
+  };
+  if (c0 < cols) {
+    const bool fast = vec && c0 + 8 <= cols;
+    int64_t r = r0 + 8 * wave + ro;
+    // groups of 8 rows (stride 32); the next group's loads are issued before
+    // the current group is reduced
+    if (r + 7 * 32 < r1) {
+      v4u a[8], b[8], na[8], nb[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) load_raw8<DT>(X + (r + 32 * u) * (int64_t)cols, c0, cols, fast, a[u], b[u]);
+      for (r += 8 * 32; r + 7 * 32 < r1; r += 8 * 32) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) load_raw8<DT>(X + (r + 32 * u) * (int64_t)cols, c0, cols, fast, na[u], nb[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          add(a[u], b[u]);
+          a[u] = na[u];
+          b[u] = nb[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) add(a[u], b[u]);
+    }
+    for (; r < r1; r += 32) {
+      v4u a, b;
+      load_raw8<DT>(X + r * (int64_t)cols, c0, cols, fast, a, b);
+      add(a, b);
+    }
+  }
+  // lanes with the same chunk: xor over the row-offset bits of the lane id
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+#pragma unroll
+    for (int d = 0; d < NW; ++d) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)m[d], off, 64);
+      if constexpr (DT == DT_F32) m[d] = max(m[d], o);
+      else m[d] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, m[d]),
+                                                                         __builtin_bit_cast(us2, o)));
+    }
+  }
+  if (ro == 0)
+#pragma unroll
+    for (int d = 0; d < NW; ++d) sm[wave][cc][d] = m[d];
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    uint32_t byte = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t mm = 0u;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t v;
+        if constexpr (DT == DT_F32) v = sm[w][cc][e];
+        else v = (sm[w][cc][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        mm = max(mm, v);
+      }
+      if (c0 + e < cols && mag_to_half_value<DT>(mm) > tau) byte |= 1u << e;
+    }
+    // lanes 0..3 -> word 2 bx (columns 0..31 of the group), lanes 4..7 -> word 2 bx + 1
+    uint32_t word = byte << (8 * (cc & 3));
+    word |= (uint32_t)__shfl_xor((int)word, 1, 64);
+    word |= (uint32_t)__shfl_xor((int)word, 2, 64);
+    const int w = blockIdx.x * 2 + (cc >> 2);
+    if ((cc & 3) == 0 && w < nwords) bits[(int64_t)blockIdx.y * nwords + w] = word;
   }
 }
 
-// Row quantization: one wave per row, a wave walks rows row0, row0 + W, ...
-// (W waves in the grid). VEC rows (cols % 8 == 0, 16-byte aligned) are read
-// with 16-byte loads and written with 8-byte stores; with NCH > 0 a row of at
-// most 64 * NCH chunks stays in registers between the absmax and the
-// quantization, otherwise it streams twice through the cache. The column
-// bitmask is staged in LDS.
+// ---------------------------------------------------------------------------
+// Row quantization. Prologue of every workgroup (tau on): column mask = OR
+// of the slab words, exclusive per-word popcount prefix, both in LDS;
+// workgroup 0 writes the ascending outlier list (first cap entries) and the
+// count. Then one wave per row, a wave walks rows row0, row0 + W, ... (W
+// waves in the grid). VEC rows (cols % 8 == 0, 16-byte aligned) are read with
+// 16-byte loads and written with 8-byte stores; with NCH > 0 a row of at most
+// 64 * NCH chunks stays in registers between the absmax and the quantization,
+// otherwise it streams twice through the cache.
+//
+// Quantization of one element: x16 = fp16(x), p = fl32(x16 * inv),
+// code = rint(p). For a non-outlier column |x16| <= s, and fl32(s * fl32(127 /
+// s)) rounds to 127 for every fp16 value s, so |code| <= 127 and the clamp to
+// [-127, 127] never applies. rint is computed as fl32(p + 1.5 * 2^23), whose
+// low byte is the two's-complement code; contraction into an FMA is off so
+// that the product is rounded to fp32 first.
 template <int DT, int NCH, bool VEC>
 __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __restrict__ X, int64_t rows,
-                                                  int cols, int tau_on, const uint32_t* __restrict__ gmask,
-                                                  const int32_t* __restrict__ prefix, int8_t* __restrict__ codes,
-                                                  float* __restrict__ scale, uint16_t* __restrict__ sub, int cap) {
+                                                  int cols, int tau_on, const uint32_t* __restrict__ bits,
+                                                  int slabs, int8_t* __restrict__ codes, float* __restrict__ scale,
+                                                  int32_t* __restrict__ idx, int32_t* __restrict__ count,
+                                                  uint16_t* __restrict__ sub, int cap) {
+#pragma clang fp contract(off)
   typedef typename Elem<DT>::T T;
-  extern __shared__ uint32_t smask[];
+  extern __shared__ uint32_t smem_q[];
+  __shared__ int wsum[4];
   const int nwords = (cols + 31) >> 5;
-  if (tau_on)
-    for (int w = threadIdx.x; w < nwords; w += 256) smask[w] = gmask[w];
-  __syncthreads();
+  uint32_t* smask = smem_q;
+  int32_t* sprefix = reinterpret_cast<int32_t*>(smem_q + nwords);
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
 
-  const int lane = threadIdx.x & 63;
   const int64_t wstride = (int64_t)gridDim.x * 4;
-  const int64_t row0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row0 = (int64_t)blockIdx.x * 4 + wid;
   const int nchunk = (cols + 7) >> 3;
-
-  auto chunk_mask = [&](int ci) -> uint32_t {
-    if (!tau_on) return 0u;
-    const int c0 = ci * 8;
-    return (smask[c0 >> 5] >> (c0 & 31)) & 0xffu;
-  };
   auto load = [&](const T* xr, int ci, v4u& a, v4u& b) {
     if constexpr (VEC) {
       a = *reinterpret_cast<const v4u*>(xr + ci * 8);
@@ -320,94 +247,262 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
       load_raw8<DT>(xr, ci * 8, cols, false, a, b);
     }
   };
-  auto absmax = [&](const v4u& a, const v4u& b, uint32_t om) -> uint32_t {
-    uint32_t mx = 0u;
+  // slab words of this thread's first column word, requested before the row
+  // data (memory requests of a wave complete in order)
+  uint32_t sw[CF_MAX_SLABS];
+  const bool w0ok = tau_on && t < nwords;
+  if (w0ok) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t m = chunk_mag<DT>(a, b, e);
-      mx = ((om >> e) & 1u) ? mx : max(mx, m);
-    }
-    return mx;
-  };
-  auto emit = [&](int64_t row, int ci, const v4u& a, const v4u& b, float inv) {
-    const int c0 = ci * 8;
-    const uint32_t om = chunk_mask(ci);
-    uint32_t q[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float r = rintf(chunk_val<DT>(a, b, e) * inv);
-      r = __builtin_amdgcn_fmed3f(r, -127.0f, 127.0f);
-      const uint32_t c = ((om >> e) & 1u) ? 0u : ((uint32_t)(int)r & 0xffu);
-      q[e >> 2] |= c << (8 * (e & 3));
-    }
-    int8_t* cr = codes + row * (int64_t)cols + c0;
-    if constexpr (VEC) {
-      *reinterpret_cast<v2u*>(cr) = v2u{q[0], q[1]};
-    } else {
-      for (int e = 0; e < 8; ++e)
-        if (c0 + e < cols) cr[e] = (int8_t)((q[e >> 2] >> (8 * (e & 3))) & 0xffu);
-    }
-    if (om) put_outliers<DT>(sub + row * (int64_t)cap, smask, prefix, c0, om, a, b, cap);
-  };
-  auto finish = [&](uint32_t mx, float& s, float& inv) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-    s = mag_to_half_value<DT>(mx);        // max |fp16(x)| = fp16 cast of the max magnitude
-    inv = (s > 0.0f) ? (127.0f / s) : 0.0f;
-  };
-
-  for (int64_t row = row0; row < rows; row += wstride) {
-    const T* xr = X + row * (int64_t)cols;
-    uint32_t mx = 0u;
-    float sv, inv;
-    if constexpr (NCH > 0) {
-      v4u ra[NCH], rb[NCH];
+    for (int sl = 0; sl < CF_MAX_SLABS; ++sl) sw[sl] = sl < slabs ? bits[(int64_t)sl * nwords + t] : 0u;
+  }
+  // the first row of a register-resident wave is requested before the
+  // prologue, so that its memory latency overlaps the mask construction
+  constexpr int NR = NCH > 0 ? NCH : 1;
+  v4u ra[NR], rb[NR];
+  if constexpr (NCH > 0) {
+    if (row0 < rows) {
+      const T* xr = X + row0 * (int64_t)cols;
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         const int ci = i * 64 + lane;
         if (ci < nchunk) load(xr, ci, ra[i], rb[i]);
       }
+    }
+  }
+
+  if (tau_on) {
+    if (w0ok) {
+      uint32_t mw = 0u;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int ci = i * 64 + lane;
-        if (ci < nchunk) mx = max(mx, absmax(ra[i], rb[i], chunk_mask(ci)));
-      }
-      finish(mx, sv, inv);
+      for (int sl = 0; sl < CF_MAX_SLABS; ++sl) mw |= sw[sl];
+      smask[t] = mw;
+    }
+    for (int w = t + 256; w < nwords; w += 256) {
+      uint32_t v[CF_MAX_SLABS];
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int ci = i * 64 + lane;
-        if (ci < nchunk) emit(row, ci, ra[i], rb[i], inv);
+      for (int sl = 0; sl < CF_MAX_SLABS; ++sl) v[sl] = sl < slabs ? bits[(int64_t)sl * nwords + w] : 0u;
+      uint32_t mw = 0u;
+#pragma unroll
+      for (int sl = 0; sl < CF_MAX_SLABS; ++sl) mw |= v[sl];
+      smask[w] = mw;
+    }
+    __syncthreads();
+    const int per = (nwords + 255) / 256;
+    const int w0 = t * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+      if (w0 + i < nwords) local += __popc(smask[w0 + i]);
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int i = 0; i < wid; ++i) run += wsum[i];
+    for (int i = 0; i < per; ++i) {
+      const int w = w0 + i;
+      if (w >= nwords) break;
+      sprefix[w] = run;
+      uint32_t mw = smask[w];
+      if (blockIdx.x == 0) {
+        int j = run;
+        while (mw) {
+          const int b = __ffs(mw) - 1;
+          if (j < cap) idx[j] = w * 32 + b;
+          ++j;
+          mw &= mw - 1u;
+        }
       }
+      run += __popc(smask[w]);
+    }
+    if (blockIdx.x == 0 && t == 0) *count = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  } else if (blockIdx.x == 0 && t == 0) {
+    *count = 0;
+  }
+
+  auto chunk_mask = [&](int ci) -> uint32_t {
+    if (!tau_on) return 0u;
+    const int c0 = ci * 8;
+    return (smask[c0 >> 5] >> (c0 & 31)) & 0xffu;
+  };
+  // largest magnitude (storage-format bits) of the chunk's non-outlier elements;
+  // any: some lane of the wave has an outlier column in this chunk (uniform)
+  auto absmax = [&](const v4u& a, const v4u& b, uint32_t om, bool any) -> uint32_t {
+    if constexpr (VEC && DT != DT_F32) {
+      us2 mx = {0, 0};
+      if (!any) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, a[d] & 0x7fff7fffu));
+      } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t keep = (((om >> (2 * d)) & 1u) ? 0u : 0x0000ffffu) | (((om >> (2 * d + 1)) & 1u) ? 0u : 0xffff0000u);
+          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, a[d] & 0x7fff7fffu & keep));
+        }
+      }
+      return max((uint32_t)mx[0], (uint32_t)mx[1]);
     } else {
-      for (int cb = 0; cb < nchunk; cb += 4 * 64) {
-        v4u a[4], b[4];
+      uint32_t mx = 0u;
+      if (!any) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ci = cb + u * 64 + lane;
-          if (ci < nchunk) load(xr, ci, a[u], b[u]);
-        }
+        for (int e = 0; e < 8; ++e) mx = max(mx, chunk_mag<DT>(a, b, e));
+      } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ci = cb + u * 64 + lane;
-          if (ci < nchunk) mx = max(mx, absmax(a[u], b[u], chunk_mask(ci)));
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t m = chunk_mag<DT>(a, b, e);
+          mx = ((om >> e) & 1u) ? mx : max(mx, m);
         }
       }
-      finish(mx, sv, inv);
-      for (int cb = 0; cb < nchunk; cb += 4 * 64) {
-        v4u a[4], b[4];
+      return mx;
+    }
+  };
+  // codes of one chunk, packed little-endian into two words
+  auto quant8 = [&](const v4u& a, const v4u& b, float inv, uint32_t& lo, uint32_t& hi) {
+    uint32_t h[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ci = cb + u * 64 + lane;
-          if (ci < nchunk) load(xr, ci, a[u], b[u]);
-        }
+    for (int d = 0; d < 4; ++d) {
+      if constexpr (DT == DT_F16) h[d] = a[d];
+      else if constexpr (DT == DT_BF16) h[d] = bf16x2_to_f16x2(a[d]);
+      else h[d] = f32x2_to_f16x2(__uint_as_float(d < 2 ? a[2 * d] : b[2 * d - 4]),
+                                 __uint_as_float(d < 2 ? a[2 * d + 1] : b[2 * d - 3]));
+    }
+    uint32_t q[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ci = cb + u * 64 + lane;
-          if (ci < nchunk) emit(row, ci, a[u], b[u], inv);
-        }
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)(h[e >> 1] >> (16 * (e & 1))));
+      const float p = (float)x * inv;
+      q[e] = __float_as_uint(p + 12582912.0f);
+    }
+    lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u) | __builtin_amdgcn_perm(q[3], q[2], 0x04000c0cu);
+    hi = __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u) | __builtin_amdgcn_perm(q[7], q[6], 0x04000c0cu);
+  };
+  auto emit = [&](int64_t row, int ci, const v4u& a, const v4u& b, float inv, uint32_t om, bool any) {
+    const int c0 = ci * 8;
+    uint32_t lo, hi;
+    quant8(a, b, inv, lo, hi);
+    if (any && om) {
+      // outlier columns: code 0 (byte mask), value to the dense sub-matrix
+      uint32_t kl = 0u, kh = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kl |= ((om >> e) & 1u) ? 0u : (0xffu << (8 * e));
+        kh |= ((om >> (e + 4)) & 1u) ? 0u : (0xffu << (8 * e));
+      }
+      lo &= kl;
+      hi &= kh;
+      // rank of column c among the outlier columns: prefix of its word plus the
+      // set bits below it
+      uint16_t* srow = sub + row * (int64_t)cap;
+      const int w = c0 >> 5;
+      const uint32_t mw = smask[w];
+      const int base = sprefix[w];
+      uint32_t rest = om;
+      while (rest) {
+        const int e = __ffs(rest) - 1;
+        rest &= rest - 1u;
+        const int c = c0 + e;
+        const int j = base + __popc(mw & ((1u << (c & 31)) - 1u));
+        if (j < cap) srow[j] = __builtin_bit_cast(uint16_t, (_Float16)chunk_val<DT>(a, b, e));
       }
     }
-    if (lane == 0) scale[row] = sv;
+    int8_t* cr = codes + row * (int64_t)cols + c0;
+    if constexpr (VEC) {
+      *reinterpret_cast<v2u*>(cr) = v2u{lo, hi};
+    } else {
+      for (int e = 0; e < 8; ++e)
+        if (c0 + e < cols) cr[e] = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xffu);
+    }
+  };
+  auto finish = [&](uint32_t mx, float& s, float& inv) {
+    mx = wave_umax(mx);
+    s = mag_to_half_value<DT>(mx);        // max |fp16(x)| = fp16 cast of the max magnitude
+    inv = (s > 0.0f) ? (127.0f / s) : 0.0f;
+  };
+
+  // the outlier columns are the same for every row: a wave-uniform flag per
+  // register chunk (once per wave) lets the common case skip all masking; the
+  // chunk masks themselves are re-read from LDS only where a flag is set
+  uint32_t anyb = 0u;
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ci = i * 64 + lane;
+      const uint32_t om = ci < nchunk ? chunk_mask(ci) : 0u;
+      if (__builtin_amdgcn_ballot_w64(om != 0u) != 0) anyb |= 1u << i;
+    }
+  }
+  auto rmask = [&](int i) -> uint32_t {
+    const int ci = i * 64 + lane;
+    return ((anyb >> i) & 1u) && ci < nchunk ? chunk_mask(ci) : 0u;
+  };
+
+  if constexpr (NCH > 0) {
+    for (int64_t row = row0; row < rows; row += wstride) {
+      if (row != row0) {
+        const T* xr = X + row * (int64_t)cols;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int ci = i * 64 + lane;
+          if (ci < nchunk) load(xr, ci, ra[i], rb[i]);
+        }
+      }
+      uint32_t mx = 0u;
+      float sv, inv;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ci = i * 64 + lane;
+        if (ci < nchunk) mx = max(mx, absmax(ra[i], rb[i], rmask(i), (anyb >> i) & 1u));
+      }
+      finish(mx, sv, inv);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ci = i * 64 + lane;
+        if (ci < nchunk) emit(row, ci, ra[i], rb[i], inv, rmask(i), (anyb >> i) & 1u);
+      }
+      if (lane == 0) scale[row] = sv;
+    }
+  } else {
+    for (int64_t row = row0; row < rows; row += wstride) {
+      const T* xr = X + row * (int64_t)cols;
+      uint32_t mx = 0u;
+      float sv, inv;
+        for (int cb = 0; cb < nchunk; cb += 4 * 64) {
+          v4u a[4], b[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ci = cb + u * 64 + lane;
+            if (ci < nchunk) load(xr, ci, a[u], b[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ci = cb + u * 64 + lane;
+            const uint32_t om = ci < nchunk ? chunk_mask(ci) : 0u;
+            const bool any = __builtin_amdgcn_ballot_w64(om != 0u) != 0;
+            if (ci < nchunk) mx = max(mx, absmax(a[u], b[u], om, any));
+          }
+        }
+        finish(mx, sv, inv);
+        for (int cb = 0; cb < nchunk; cb += 4 * 64) {
+          v4u a[4], b[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ci = cb + u * 64 + lane;
+            if (ci < nchunk) load(xr, ci, a[u], b[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ci = cb + u * 64 + lane;
+            const uint32_t om = ci < nchunk ? chunk_mask(ci) : 0u;
+            const bool any = __builtin_amdgcn_ballot_w64(om != 0u) != 0;
+            if (ci < nchunk) emit(row, ci, a[u], b[u], inv, om, any);
+          }
+        }
+      if (lane == 0) scale[row] = sv;
+    }
   }
 }
 
@@ -418,9 +513,8 @@ static bool aligned(const void* p, int a) { return ((uintptr_t)p % (uintptr_t)a)
 
 size_t quant_scratch_words(int64_t rows, int64_t cols) {
   const int64_t nw = (cols + 31) / 32;
-  const int64_t slabs = rows < FLAG_SLABS ? (rows > 0 ? rows : 1) : FLAG_SLABS;
-  // bits[slabs][nw] + mask[nw] + prefix[nw]
-  return (size_t)((slabs + 2) * (nw > 0 ? nw : 1));
+  // bits[slabs][nw]
+  return (size_t)(colflag_slabs(rows, cols) * (nw > 0 ? nw : 1));
 }
 
 template <int DT>
@@ -429,46 +523,46 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
                                     uint32_t* scratch, hipStream_t st) {
   typedef typename Elem<DT>::T T;
   const T* X = static_cast<const T*>(Xv);
-  const bool tau_on = (tau > 0.0f) && (tau < __builtin_huge_valf());
+  const bool tau_on = (tau > 0.0f) && (tau < __builtin_huge_valf()) && rows > 0 && cols > 0;
   const int nwords = (cols + 31) / 32;
   const int vec = (cols % 8 == 0) && aligned(X, 16) && aligned(codes, 8);
-  const int64_t slabs = tau_on ? (rows < FLAG_SLABS ? (rows > 0 ? rows : 1) : FLAG_SLABS) : 0;
-  const int64_t nw1 = nwords > 0 ? nwords : 1;
-  uint32_t* bits = scratch;
-  uint32_t* mask = scratch + (size_t)(rows < FLAG_SLABS ? (rows > 0 ? rows : 1) : FLAG_SLABS) * nw1;
-  int32_t* prefix = reinterpret_cast<int32_t*>(mask + nw1);
-  if (tau_on && rows > 0 && cols > 0) {
-    // about 1024 workgroups, at least 32 rows per slab (8 per wave)
-    const int gx = (cols + FLAG_COLS - 1) / FLAG_COLS;
-    int64_t want = (1024 + gx - 1) / gx;
-    if (want > slabs) want = slabs;
-    int64_t rps = (rows + want - 1) / want;
-    if (rps < 32) rps = 32;
-    const int64_t gy = (rows + rps - 1) / rps;
-    hipLaunchKernelGGL(k_outlier_flags<DT>, dim3(gx, (unsigned)gy), dim3(256), 0, st, X, rows, cols, tau, rps, vec,
-                       nwords, bits);
-    hipLaunchKernelGGL(k_outlier_compact, dim3(1), dim3(1024), 0, st, bits, (int)gy, nwords, mask, prefix, idx, cap,
-                       count);
-  } else {
-    // no split: empty list, count 0, and no mask reads (tau_on = 0 below)
-    hipLaunchKernelGGL(k_outlier_compact, dim3(1), dim3(1024), 0, st, bits, 0, 0, mask, prefix, idx, cap, count);
+  const int slabs = colflag_slabs(rows, cols);
+  if (tau_on) {
+    const int gx = (cols + CF_COLS - 1) / CF_COLS;
+    const int64_t rps = (rows + slabs - 1) / slabs;
+    hipLaunchKernelGGL(k_colflags<DT>, dim3(gx, (unsigned)slabs), dim3(256), 0, st, X, rows, cols, tau, rps, vec,
+                       nwords, scratch);
   }
-  if (rows > 0) {
-    const int nchunk = (cols + 7) / 8;
-    const size_t lds = tau_on ? (size_t)nw1 * 4 : 0;
-    const dim3 grid((unsigned)((rows + 3) / 4));   // one row per wave, four waves per workgroup
-#define I8L_RQ(NCH, VEC)                                                                                   \
-  hipLaunchKernelGGL((k_rowquant<DT, NCH, VEC>), grid, dim3(256), lds, st, X, rows, cols, (int)tau_on, mask, \
-                     prefix, codes, scale, sub, cap)
-    if (vec) {
-      if (nchunk <= 64 * 8) I8L_RQ(8, true);
-      else I8L_RQ(0, true);
-    } else {
-      if (nchunk <= 64 * 8) I8L_RQ(8, false);
-      else I8L_RQ(0, false);
+  // the row kernel also writes the outlier list and count (count 0 when the split is off)
+  const int64_t rblocks = rows > 0 ? (rows + 3) / 4 : 1;
+  dim3 grid((unsigned)(rblocks < RQ_MAX_BLOCKS ? rblocks : RQ_MAX_BLOCKS));
+  const int nchunk = (cols + 7) / 8;
+  const size_t lds = tau_on ? (size_t)2 * (nwords > 0 ? nwords : 1) * 4 : 0;
+  // mask + prefix of the widest rows (I8L_MAX_COLS) take 64 KB of LDS
+#define I8L_RQ(NCH, VEC)                                                                                        \
+  do {                                                                                                          \
+    auto kern = k_rowquant<DT, NCH, VEC>;                                                                       \
+    if (lds > 32768) {                                                                                          \
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e != hipSuccess) return e;                                                                            \
+    }                                                                                                           \
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, X, rows, cols, (int)tau_on, scratch, slabs, codes, scale,  \
+                       idx, count, sub, cap);                                                                   \
+  } while (0)
+  // rows of up to 4096 16-bit values stay in registers; fp32, wider, unaligned
+  // or ragged rows use the streaming path (fewer registers)
+  bool done = false;
+  if constexpr (DT != DT_F32) {
+    if (vec && nchunk <= 64 * 8) {
+      I8L_RQ(8, true);
+      done = true;
     }
-#undef I8L_RQ
   }
+  if (!done) {
+    if (vec) I8L_RQ(0, true);
+    else I8L_RQ(0, false);
+  }
+#undef I8L_RQ
   return hipGetLastError();
 }
 

@@ -30,10 +30,18 @@ namespace i8l {
 // 32 x 32 (n x m); lane (lr, lg) holds, for tile (i, j) and register r,
 //   n = nw + i*32 + (r/4)*8 + lg*4 + r%4,   m = mw + j*32 + lr.
 //
+// opan (optional): LDS panels of the first 16 outlier columns for a 256 x 256
+// block tile with origin (tm0, tn0): P[n][16] = Wdq[n, O[j]] at opan, then
+// Q[m][16] = subA[m, j] at opan + OPAN_Q (fp16, 32 bytes per row, zero past
+// the count); filled by the kernel before its k loop.
+//
 // With LDS_OUT (16-bit outputs, eight waves over a 256 x 256 block tile whose
 // origin is (tm0, tn0)), the results are written to the LDS tile `ot` (row m,
 // 16-byte chunk of 8 features) instead of global memory; the caller then
 // stores whole rows with otile_store. The call starts with a block barrier.
+constexpr int OPAN_Q = 256 * 32;      // Q panel after the 256 x 16 P panel
+constexpr int OPAN_BYTES = 2 * 256 * 32;
+
 template <int TI, int TJ, int DT, bool OV, bool LDS_OUT = false>
 __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw, int lr, int lg, int M, int N, int K,
                                              const float* __restrict__ SCA, const int8_t* __restrict__ CB,
@@ -42,7 +50,8 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
                                              const int32_t* __restrict__ count,
                                              const typename Elem<DT>::T* __restrict__ bias,
                                              typename Elem<DT>::T* __restrict__ out, int32_t* __restrict__ c32,
-                                             char* ot = nullptr, int tm0 = 0, int tn0 = 0) {
+                                             char* ot = nullptr, int tm0 = 0, int tn0 = 0,
+                                             const char* opan = nullptr) {
   static_assert(!LDS_OUT || DT != DT_F32, "LDS output staging holds 16-bit values");
   if constexpr (LDS_OUT) __syncthreads();   // the operand stages are no longer read
   typedef typename Elem<DT>::T T;
@@ -101,8 +110,19 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
       for (int r = 0; r < 16; ++r)
         accf[j][r] = (float)acc[i][j][r] * ((sa[j] * sb[r]) * (1.0f / 16129.0f));
 
-    // outlier columns: fp16 product accumulated into the same fp32 registers
-    for (int jo = 0; jo < cnt; jo += 16) {
+    // outlier columns: fp16 product accumulated into the same fp32 registers;
+    // the first 16 columns come from the LDS panels when the kernel staged them
+    int jo = 0;
+    if (opan != nullptr && cnt > 0) {
+      const v8h P = *reinterpret_cast<const v8h*>(opan + (nw - tn0 + i * 32 + lr) * 32 + lg * 16);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const v8h Q = *reinterpret_cast<const v8h*>(opan + OPAN_Q + (mw - tm0 + j * 32 + lr) * 32 + lg * 16);
+        accf[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P, Q, accf[j], 0, 0, 0);
+      }
+      jo = 16;
+    }
+    for (; jo < cnt; jo += 16) {
       v8h P, Q[TJ];
       const int n = nw + i * 32 + lr;
       const bool nok = n < N;
@@ -526,10 +546,44 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   const int nk = (K + BK - 1) / BK;
   load_b(0);
   load_a(0);
+
+  // outlier panels (first 16 outlier columns) for the epilogue, gathered while
+  // the first operand tiles are in flight: thread t covers row t >> 1 of the
+  // tile, columns 8 (t & 1) .. +7, of both panels
+  char* opan = reinterpret_cast<char*>(smem) + 2 * STAGE;
+  int o16 = 0;
+  if (count != nullptr) o16 = min(min(*count, cap), 16);
+  const int orow = tid >> 1, oj = (tid & 1) * 8;
+  int pbyte[8];
+  uint16_t qval[8];
+  float psc = 0.0f;
+  if (o16 > 0) {
+    const int n = n0 + orow, m = m0 + orow;
+    const bool nok = n < N, mok = m < M;
+    psc = nok ? SCB[n] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = oj + e;
+      pbyte[e] = (nok && j < o16) ? (int)CB[(int64_t)n * K + idx[j]] : 0;
+      qval[e] = (mok && j < o16) ? subA[(int64_t)m * cap + j] : (uint16_t)0;
+    }
+  }
+
   write_b(0);
   write_a(0);
   load_b(BK);
   load_a(BK);
+  if (o16 > 0) {
+    const float sig = psc * (1.0f / 127.0f);
+    v8h P, Q;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      P[e] = (_Float16)((float)pbyte[e] * sig);
+      Q[e] = __builtin_bit_cast(_Float16, qval[e]);
+    }
+    *reinterpret_cast<v8h*>(opan + orow * 32 + oj * 2) = P;
+    *reinterpret_cast<v8h*>(opan + OPAN_Q + orow * 32 + oj * 2) = Q;
+  }
   __syncthreads();
   fread(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
@@ -579,14 +633,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
     fread(st ^ 1, 0, 0);
   }
 
+  const char* op = o16 > 0 ? opan : nullptr;
   if constexpr (DT == DT_F32) {
     fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 64, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, idx,
-                                 count, bias, out, c32);
+                                 count, bias, out, c32, nullptr, m0, n0, op);
   } else {
     // output tile through LDS, stored as whole rows
     char* ot = reinterpret_cast<char*>(smem);
     fwd_epilogue<TI, TJ, DT, OV, true>(acc, m0 + wm * 64, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap,
-                                       idx, count, bias, out, c32, ot, m0, n0);
+                                       idx, count, bias, out, c32, ot, m0, n0, op);
     __syncthreads();
     otile_store<typename Elem<DT>::T>(ot, out, N, m0, n0, M, N, wave, lane);
   }
@@ -597,7 +652,7 @@ static hipError_t launch_fwd_w8(const int8_t* CA, const float* SCA, int M, const
                                 int N, int K, const uint16_t* subA, int cap, const int32_t* idx,
                                 const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   typedef typename Elem<DT>::T T;
-  constexpr size_t lds = (size_t)2 * (256 + 256) * 128;
+  constexpr size_t lds = (size_t)2 * (256 + 256) * 128 + OPAN_BYTES;   // two stages + outlier panels
   auto kern = k_gemm_fwd_w8<DT, OV>;
   static bool attr_set = false;
   if (!attr_set) {

@@ -41,6 +41,10 @@ namespace i8l {
 // stores whole rows with otile_store. The call starts with a block barrier.
 constexpr int OPAN_Q = 256 * 32;      // Q panel after the 256 x 16 P panel
 constexpr int OPAN_BYTES = 2 * 256 * 32;
+// lsc (optional): the block tile's SCB[n0 + 0..255], SCA[m0 + 0..255] and
+// fp32 bias[n0 + 0..255] in LDS (zero past the matrix), filled by the kernel
+// before its k loop.
+constexpr int LSC_SCB = 0, LSC_SCA = 256, LSC_BIAS = 512, LSC_BYTES = 768 * 4;
 
 template <int TI, int TJ, int DT, bool OV, bool LDS_OUT = false>
 __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw, int lr, int lg, int M, int N, int K,
@@ -51,7 +55,7 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
                                              const typename Elem<DT>::T* __restrict__ bias,
                                              typename Elem<DT>::T* __restrict__ out, int32_t* __restrict__ c32,
                                              char* ot = nullptr, int tm0 = 0, int tn0 = 0,
-                                             const char* opan = nullptr) {
+                                             const char* opan = nullptr, const float* lsc = nullptr) {
   static_assert(!LDS_OUT || DT != DT_F32, "LDS output staging holds 16-bit values");
   if constexpr (LDS_OUT) __syncthreads();   // the operand stages are no longer read
   typedef typename Elem<DT>::T T;
@@ -85,7 +89,8 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int m = mb + j * 32;
-    sa[j] = (m < M) ? SCA[m] : 0.0f;
+    if (lsc != nullptr) sa[j] = lsc[LSC_SCA + m - tm0];
+    else sa[j] = (m < M) ? SCA[m] : 0.0f;
   }
   int cnt = 0;
   if (count != nullptr) {
@@ -97,10 +102,19 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
     float sb[16];
+    if (lsc != nullptr) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
-      sb[r] = (n < N) ? SCB[n] : 0.0f;
+      for (int q = 0; q < 4; ++q) {
+        const v4f v = *reinterpret_cast<const v4f*>(lsc + LSC_SCB + nb - tn0 + i * 32 + q * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sb[4 * q + e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
+        sb[r] = (n < N) ? SCB[n] : 0.0f;
+      }
     }
     // (SCA * SCB) * fl32(1/127^2): exactly 1 when both scales are 127
     v16f accf[TJ];
@@ -150,10 +164,19 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
 
     // bias, cast, store
     float bv[16];
+    if (lsc != nullptr) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
-      bv[r] = (bias != nullptr && n < N) ? Elem<DT>::to_f32(bias[n]) : 0.0f;
+      for (int q = 0; q < 4; ++q) {
+        const v4f v = *reinterpret_cast<const v4f*>(lsc + LSC_BIAS + nb - tn0 + i * 32 + q * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[4 * q + e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
+        bv[r] = (bias != nullptr && n < N) ? Elem<DT>::to_f32(bias[n]) : 0.0f;
+      }
     }
     if constexpr (LDS_OUT) {
 #pragma unroll
@@ -569,10 +592,31 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
     }
   }
 
+  // the tile's scales and bias, likewise (thread t < 256: column n0 + t,
+  // thread t >= 256: row m0 + t - 256)
+  float* lsc = reinterpret_cast<float*>(opan + OPAN_BYTES);
+  float sc0 = 0.0f, bias0 = 0.0f;
+  if (tid < 256) {
+    const int n = n0 + tid;
+    if (n < N) {
+      sc0 = SCB[n];
+      if (bias != nullptr) bias0 = Elem<DT>::to_f32(bias[n]);
+    }
+  } else {
+    const int m = m0 + tid - 256;
+    if (m < M) sc0 = SCA[m];
+  }
+
   write_b(0);
   write_a(0);
   load_b(BK);
   load_a(BK);
+  if (tid < 256) {
+    lsc[LSC_SCB + tid] = sc0;
+    lsc[LSC_BIAS + tid] = bias0;
+  } else {
+    lsc[LSC_SCA + tid - 256] = sc0;
+  }
   if (o16 > 0) {
     const float sig = psc * (1.0f / 127.0f);
     v8h P, Q;
@@ -636,12 +680,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   const char* op = o16 > 0 ? opan : nullptr;
   if constexpr (DT == DT_F32) {
     fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 64, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, idx,
-                                 count, bias, out, c32, nullptr, m0, n0, op);
+                                 count, bias, out, c32, nullptr, m0, n0, op, lsc);
   } else {
     // output tile through LDS, stored as whole rows
     char* ot = reinterpret_cast<char*>(smem);
     fwd_epilogue<TI, TJ, DT, OV, true>(acc, m0 + wm * 64, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap,
-                                       idx, count, bias, out, c32, ot, m0, n0, op);
+                                       idx, count, bias, out, c32, ot, m0, n0, op, lsc);
     __syncthreads();
     otile_store<typename Elem<DT>::T>(ot, out, N, m0, n0, M, N, wave, lane);
   }
@@ -652,7 +696,7 @@ static hipError_t launch_fwd_w8(const int8_t* CA, const float* SCA, int M, const
                                 int N, int K, const uint16_t* subA, int cap, const int32_t* idx,
                                 const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   typedef typename Elem<DT>::T T;
-  constexpr size_t lds = (size_t)2 * (256 + 256) * 128 + OPAN_BYTES;   // two stages + outlier panels
+  constexpr size_t lds = (size_t)2 * (256 + 256) * 128 + OPAN_BYTES + LSC_BYTES;   // stages, panels, scales
   auto kern = k_gemm_fwd_w8<DT, OV>;
   static bool attr_set = false;
   if (!attr_set) {

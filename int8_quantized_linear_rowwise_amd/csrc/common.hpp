@@ -39,14 +39,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (inputs are finite in this library;
-// NaN is kept a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (NaN stays NaN): the language
+// conversion, one v_cvt_pk_bf16_f32 on gfx950. Only the scalar form is used;
+// its result equals the bias-and-truncate rounding for every fp32 input.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Element type traits: load 8 consecutive elements as fp32 values of their
 // fp16 cast (the fp16 cast is exact for fp16 and RNE for fp32 / bf16).

@@ -116,13 +116,31 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
         sb[r] = (n < N) ? SCB[n] : 0.0f;
       }
     }
-    // (SCA * SCB) * fl32(1/127^2): exactly 1 when both scales are 127
+    // bias first (it joins the accumulator before the outlier product)
+    float bv[16];
+    if (lsc != nullptr) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f v = *reinterpret_cast<const v4f*>(lsc + LSC_BIAS + nb - tn0 + i * 32 + q * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[4 * q + e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
+        bv[r] = (bias != nullptr && n < N) ? Elem<DT>::to_f32(bias[n]) : 0.0f;
+      }
+    }
+    // C32 * (SCA * (SCB * fl32(1/127^2))) + bias in one fused multiply-add;
+    // the scale product is exactly 1 when both scales are 127
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sb[r] *= (1.0f / 16129.0f);
     v16f accf[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        accf[j][r] = (float)acc[i][j][r] * ((sa[j] * sb[r]) * (1.0f / 16129.0f));
+      for (int r = 0; r < 16; ++r) accf[j][r] = __builtin_fmaf((float)acc[i][j][r], sa[j] * sb[r], bv[r]);
 
     // outlier columns: fp16 product accumulated into the same fp32 registers;
     // the first 16 columns come from the LDS panels when the kernel staged them
@@ -162,22 +180,7 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
       for (int j = 0; j < TJ; ++j) accf[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P, Q[j], accf[j], 0, 0, 0);
     }
 
-    // bias, cast, store
-    float bv[16];
-    if (lsc != nullptr) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const v4f v = *reinterpret_cast<const v4f*>(lsc + LSC_BIAS + nb - tn0 + i * 32 + q * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[4 * q + e] = v[e];
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
-        bv[r] = (bias != nullptr && n < N) ? Elem<DT>::to_f32(bias[n]) : 0.0f;
-      }
-    }
+    // cast, store
     if constexpr (LDS_OUT) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
@@ -188,9 +191,9 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
           v2u w;
 #pragma unroll
           for (int e = 0; e < 2; ++e)
-            w[e] = (uint32_t)__builtin_bit_cast(uint16_t, Elem<DT>::from_f32(accf[j][4 * q + 2 * e] + bv[4 * q + 2 * e])) |
+            w[e] = (uint32_t)__builtin_bit_cast(uint16_t, Elem<DT>::from_f32(accf[j][4 * q + 2 * e])) |
                    ((uint32_t)__builtin_bit_cast(uint16_t,
-                                                 Elem<DT>::from_f32(accf[j][4 * q + 2 * e + 1] + bv[4 * q + 2 * e + 1]))
+                                                 Elem<DT>::from_f32(accf[j][4 * q + 2 * e + 1]))
                     << 16);
           *reinterpret_cast<v2u*>(ot + otile_off(row, chunk) + 8 * lg) = w;
         }
@@ -207,7 +210,7 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
         T* p = out + (int64_t)m * N + n;
         T v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = Elem<DT>::from_f32(accf[j][4 * q + e] + bv[4 * q + e]);
+        for (int e = 0; e < 4; ++e) v[e] = Elem<DT>::from_f32(accf[j][4 * q + e]);
         if (OV && n + 3 < N) {
           if constexpr (DT == DT_F32) {
             *reinterpret_cast<v4f*>(p) = v4f{v[0], v[1], v[2], v[3]};

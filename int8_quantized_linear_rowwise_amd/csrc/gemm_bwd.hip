@@ -623,45 +623,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_w8(const typename Elem<DT>:
   load_g(BNC);
   __syncthreads();
   fread(0, 0, 0);
+  // phases of one k step; the instruction interleave inside a phase is left to the
+  // compiler (measured faster than explicit scheduling groups here)
   for (int t = 0; t < nn; ++t) {
     const int st = t & 1;
     const int nc2 = (t + 2) * BNC;   // past the end: zeros
     fread(st, 1, 1);
     write_w(st ^ 1, 0);
     mma(0);
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-      I8L_SGB(SG_VALU, 5);
-    }
-    I8L_SGB(SG_MFMA, 2);
     __builtin_amdgcn_sched_barrier(0);
     fread(st, 2, 0);
     write_w(st ^ 1, 2);
     load_w(nc2);
     mma(1);
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-      I8L_SGB(SG_VALU, 5);
-      I8L_SGB(SG_VMEM_R, 2);
-    }
-    I8L_SGB(SG_MFMA, 2);
     __builtin_amdgcn_sched_barrier(0);
     fread(st, 3, 1);
     write_g(st ^ 1);
     load_g(nc2);
     mma(0);
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-      I8L_SGB(SG_VALU, 4);
-      I8L_SGB(SG_VMEM_R, 1);
-    }
-    I8L_SGB(SG_MFMA, 2);
     __builtin_amdgcn_sched_barrier(0);
     mma(1);
     __syncthreads();

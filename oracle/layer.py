@@ -44,6 +44,13 @@ Readings where the pages are silent (each also listed in the design notes):
  10. the float result is exact (float64) up to one final rounding to D;
  11. the outlier weight slice comes from the int8 weights (no fp16 copy kept);
  12. grad_bias sums the un-cast gradient and is returned in D.
+ 13. int8 backward variant (EasyDeL discussion #66: fwd_bits=8, bwd_bits=8;
+     the page only says the backward dot product is computed in 8 bits): both
+     operands carry scales constant along the contraction N. G is quantized
+     by Q with the split off (one scale per token row); the weight has a second
+     offline int8 copy, W^T (K x N) quantized by Q with the split off (one
+     scale per input feature k); grad_A = D(C32 * SG[m] * SCBt[k] / 127^2)
+     with C32 = CG . CBt^T exact; grad_bias as in reading 12.
 
 Pins: tests/test_oracle_*.py (brute force with exact rationals, closed-form
 special cases, invariants, the pages' error bounds).
@@ -198,6 +205,29 @@ def quantize_weight(W: np.ndarray, dt: str = "f32") -> tuple:
     """Offline weight quantization: Q with the outlier split off -> (CB, SCB)."""
     q = quantize_rowwise(W, dt, 0.0)
     return q["codes"], q["scale"]
+
+
+def quantize_weight_colwise(W: np.ndarray, dt: str = "f32") -> tuple:
+    """Second offline int8 copy for the int8 backward (reading 13): W^T (K x N)
+    quantized row-wise, i.e. one scale per input feature k -> (CBt, SCBt)."""
+    return quantize_weight(np.ascontiguousarray(np.asarray(W).T), dt)
+
+
+def linear_backward_input_int8(G: np.ndarray, dt: str, CBt: np.ndarray, SCBt: np.ndarray,
+                               rows=None) -> dict:
+    """int8 backward variant (EasyDeL discussion #66, bwd_bits=8; reading 13).
+
+    (CG, SG) = Q(G, split off); C32[m, k] = sum_n CG[m, n] * CBt[k, n] (exact);
+    grad_A[m, k] = D(C32 * SG[m] * SCBt[k] / 127^2), float64 then one rounding.
+    ``rows`` restricts grad_A / C32 to a subset of rows.
+    """
+    q = quantize_rowwise(G, dt, 0.0)
+    CG, SG = q["codes"], q["scale"]
+    idx = np.arange(CG.shape[0]) if rows is None else np.asarray(rows)
+    C32 = int_matmul(CG, CBt, rows=idx)
+    y = C32.astype(np.float64) * (SG[idx].astype(np.float64)[:, None]
+                                  * np.asarray(SCBt, np.float64)[None, :]) / 16129.0
+    return {"y": y, "grad_A": from_f64(y, dt), "c32": C32, "rows": idx, "q": q}
 
 
 # ----------------------------------------------------------------------------

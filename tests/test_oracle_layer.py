@@ -329,6 +329,67 @@ def test_rows_subset_matches_full():
 
 
 # --------------------------------------------------------------------------
+# int8 backward variant (EasyDeL discussion #66, bwd_bits=8; oracle reading 13)
+
+
+def test_int8_backward_integer_case_is_textbook_matmul():
+    """Integer G with +-127 in every row and integer W with +-127 in every column:
+    both quantize to themselves with scale 127, so grad_A = G @ W exactly."""
+    g = np.random.default_rng(50)
+    M, N, K = 33, 47, 58
+    G = _int_weights(g, M, N)
+    Wt = _int_weights(g, K, N)           # rows of W^T = columns of W
+    W = np.ascontiguousarray(Wt.T)
+    CBt, SCBt = oracle.quantize_weight_colwise(W)
+    assert np.array_equal(CBt, Wt.astype(np.int8)) and np.all(SCBt == 127)
+    b = oracle.linear_backward_input_int8(G, "f32", CBt, SCBt)
+    ref = G.astype(np.int64) @ W.astype(np.int64)
+    assert np.array_equal(b["c32"], ref)
+    assert np.array_equal(b["grad_A"], ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_int8_backward_brute_force(dt):
+    g = np.random.default_rng(51 + ["f16", "bf16", "f32"].index(dt))
+    for case in range(25):
+        M, K, N = int(g.integers(1, 6)), int(g.integers(1, 7)), int(g.integers(1, 6))
+        _, W, _, G = _tiny_layer(g, M, K, N, dt)
+        CBt, SCBt = oracle.quantize_weight_colwise(W)
+        b = oracle.linear_backward_input_int8(G, dt, CBt, SCBt)
+        G16 = [[Fraction(float(v)) for v in row] for row in to_half(G, dt)]
+        cg, _, sg, _, _ = bf_quantize(G16, None)
+        Wt16 = [[Fraction(float(v)) for v in row] for row in np.ascontiguousarray(W.T).astype(np.float16)]
+        cbt, _, sbt, _, _ = bf_quantize(Wt16, None)
+        assert CBt.tolist() == cbt and [Fraction(float(v)) for v in SCBt] == sbt
+        for m in range(M):
+            for k in range(K):
+                acc = sum(Fraction(cg[m][n] * cbt[k][n]) for n in range(N))
+                assert b["c32"][m, k] == acc
+                y = acc * sg[m] * sbt[k] / 16129
+                assert abs(Fraction(float(b["y"][m, k])) - y) <= abs(y) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+
+
+def test_int8_backward_error_bound_against_true_product():
+    """|y - G16 W16| <= sum_n |g| e_w + |w| e_g + e_g e_w with e_g = (1/2 + 2^-20) SG/127
+    per row and e_w = (1/2 + 2^-20) SCBt/127 per column of the result."""
+    g = np.random.default_rng(52)
+    M, N, K = 48, 256, 40
+    G = (g.standard_normal((M, N)) * 0.01).astype(np.float16)
+    W = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    CBt, SCBt = oracle.quantize_weight_colwise(W)
+    b = oracle.linear_backward_input_int8(G, "f16", CBt, SCBt)
+    gg = G.astype(np.float64)
+    w = W.astype(np.float16).astype(np.float64)                       # N x K
+    eg = (0.5 + 2 ** -20) * b["q"]["scale"].astype(np.float64) / 127
+    ew = (0.5 + 2 ** -20) * SCBt.astype(np.float64) / 127
+    bound = (np.abs(gg).sum(1)[:, None] * ew[None, :] + eg[:, None] * np.abs(w).sum(0)[None, :]
+             + N * eg[:, None] * ew[None, :])
+    err = np.abs(b["y"] - gg @ w)
+    assert np.all(err <= bound * (1 + 1e-9))
+    assert err.max() > 0.05 * bound.max()
+
+
+# --------------------------------------------------------------------------
 # error bounds against the unquantized product
 
 

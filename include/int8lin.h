@@ -145,6 +145,28 @@ int int8_linear_backward_input(const void* G, int dtype, int64_t M, int64_t N, c
                                int64_t K, void* grad_A, void* grad_bias, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * int8 backward variant (EasyDeL discussion #66, "Run and find Out": a Dense
+ * layer with fwd_bits=8, bwd_bits=8 computes its backward dot product in 8
+ * bits). Not the memory-efficient backward above: here both operands of the
+ * input-gradient product are int8, with scales constant along the
+ * contraction N:
+ *   (CG, SG)     = quantize(G, tau off)                    (row-wise, per token)
+ *   C32[m, k]    = sum_n CG[m, n] * CBt[k, n]              (exact int32)
+ *   grad_A[m, k] = D(C32 * SG[m] * SCBt[k] / 127^2)        (fp32 arithmetic)
+ *   grad_bias[n] = D(sum_m G[m, n])   on the un-cast G       (fp32 accumulate)
+ * CBt / SCBt: a second offline int8 copy of the weight, W^T (K x N, row-major)
+ * quantized with int8_quantize_rowwise and tau off (one scale per input
+ * feature k). G: M x N of `dtype`; grad_A: M x K of `dtype`; grad_bias: N of
+ * `dtype` or NULL; c32_debug: M x K int32 or NULL (exports C32).
+ * N <= I8L_MAX_K. The workspace holds CG, SG and the quantizer's scratch.
+ * ------------------------------------------------------------------------ */
+size_t int8_linear_backward_int8_workspace_bytes(int64_t M, int64_t N, int with_grad_bias);
+
+int int8_linear_backward_input_int8(const void* G, int dtype, int64_t M, int64_t N, const int8_t* CBt,
+                                    const float* SCBt, int64_t K, void* grad_A, void* grad_bias, int32_t* c32_debug,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ from ._lib import (I8L_BF16, I8L_F16, I8L_F32, I8L_MAX_K, Int8LinError, check, l
 
 __all__ = [
     "int8_quantize_rowwise", "int8_linear_forward", "int8_linear_backward_input", "quantize_weight",
+    "quantize_weight_colwise", "int8_linear_backward_input_int8", "backward_int8_workspace",
     "Int8LinearFunction", "Int8Linear", "Int8LinError", "forward_workspace", "forward_layout",
     "forward_check", "DTYPE_CODE", "I8L_MAX_K",
 ]
@@ -45,6 +46,12 @@ def _dev(t: Optional[torch.Tensor], name: str) -> int:
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr() if t.numel() > 0 else 0
+
+
+def _check_out(t: Optional[torch.Tensor], shape: tuple, dtype: torch.dtype, name: str) -> None:
+    """Caller-provided result tensors must have exactly the size the kernels write."""
+    if t is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype):
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
 
 
 def _stream(device: torch.device) -> int:
@@ -88,6 +95,12 @@ def quantize_weight(W: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """Offline weight quantization (threshold off): W (N x K) -> (CB int8, SCB fp32)."""
     codes, scale, _, _, _ = int8_quantize_rowwise(W, threshold=0.0, cap=0)
     return codes, scale
+
+
+def quantize_weight_colwise(W: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Second offline weight copy for the int8 backward: W^T (K x N) quantized row-wise
+    (one scale per input feature) -> (CBt int8 K x N, SCBt fp32 K)."""
+    return quantize_weight(W.t().contiguous())
 
 
 # ----------------------------------------------------------------------------
@@ -134,6 +147,8 @@ def int8_linear_forward(A: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor, bi
     if bias is not None and (bias.shape != (N,) or bias.dtype != A.dtype):
         raise ValueError("bias must have shape (N,) and A's dtype")
     cap = K if cap is None else int(cap)
+    _check_out(out, (M, N), A.dtype, "out")
+    _check_out(c32, (M, N), torch.int32, "c32")
     if out is None:
         out = _empty((M, N), A.dtype, A.device)
     if workspace is None:
@@ -157,8 +172,10 @@ def int8_linear_backward_input(G: torch.Tensor, CB: torch.Tensor, SCB: torch.Ten
         raise ValueError("G must be 2-D")
     M, N = G.shape
     K = CB.shape[1]
-    if CB.shape[0] != N or SCB.shape != (N,):
+    if CB.dim() != 2 or CB.shape[0] != N or SCB.shape != (N,) or CB.dtype != torch.int8 or SCB.dtype != torch.float32:
         raise ValueError("CB must be N x K int8 and SCB N fp32")
+    _check_out(grad_A, (M, K), G.dtype, "grad_A")
+    _check_out(grad_bias, (N,), G.dtype, "grad_bias")
     if grad_A is None:
         grad_A = _empty((M, K), G.dtype, G.device)
     if with_grad_bias and grad_bias is None:
@@ -173,6 +190,44 @@ def int8_linear_backward_input(G: torch.Tensor, CB: torch.Tensor, SCB: torch.Ten
                                          workspace.data_ptr() if workspace is not None else 0,
                                          workspace.numel() if workspace is not None else 0, _stream(G.device)),
           "int8_linear_backward_input")
+    return grad_A, grad_bias
+
+
+def backward_int8_workspace(M: int, N: int, with_grad_bias: bool, device) -> torch.Tensor:
+    wsb = lib.int8_linear_backward_int8_workspace_bytes(M, N, int(with_grad_bias))
+    return _empty((max(wsb, 1),), torch.uint8, device)
+
+
+def int8_linear_backward_input_int8(G: torch.Tensor, CBt: torch.Tensor, SCBt: torch.Tensor,
+                                    with_grad_bias: bool = True, grad_A: Optional[torch.Tensor] = None,
+                                    grad_bias: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                    c32: Optional[torch.Tensor] = None):
+    """int8 backward variant: grad_A = D(C32 * SG * SCBt / 127^2), C32 = quantize(G) @ CBt^T in int32;
+    grad_bias = column sums of G (un-cast). CBt, SCBt come from quantize_weight_colwise."""
+    if G.dim() != 2:
+        raise ValueError("G must be 2-D")
+    M, N = G.shape
+    K = CBt.shape[0]
+    if (CBt.dim() != 2 or CBt.shape[1] != N or SCBt.shape != (K,) or CBt.dtype != torch.int8
+            or SCBt.dtype != torch.float32):
+        raise ValueError("CBt must be K x N int8 and SCBt K fp32")
+    _check_out(grad_A, (M, K), G.dtype, "grad_A")
+    _check_out(grad_bias, (N,), G.dtype, "grad_bias")
+    _check_out(c32, (M, K), torch.int32, "c32")
+    if grad_A is None:
+        grad_A = _empty((M, K), G.dtype, G.device)
+    if with_grad_bias and grad_bias is None:
+        grad_bias = _empty((N,), G.dtype, G.device)
+    if not with_grad_bias:
+        grad_bias = None
+    wsb = lib.int8_linear_backward_int8_workspace_bytes(M, N, int(grad_bias is not None))
+    if workspace is None or workspace.numel() < wsb:
+        workspace = _empty((max(wsb, 1),), torch.uint8, G.device)
+    check(lib.int8_linear_backward_input_int8(_dev(G, "G"), _code(G), M, N, _dev(CBt, "CBt"), _dev(SCBt, "SCBt"), K,
+                                              _dev(grad_A, "grad_A"), _dev(grad_bias, "grad_bias"),
+                                              _dev(c32, "c32"), workspace.data_ptr(), workspace.numel(),
+                                              _stream(G.device)),
+          "int8_linear_backward_input_int8")
     return grad_A, grad_bias
 
 

@@ -36,6 +36,9 @@ SIGNATURES = {
     "int8_linear_forward_check": (_int, [_vp, _i64, _i64, _i32, _vp, ctypes.POINTER(_i32)]),
     "int8_linear_backward_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "int8_linear_backward_input": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "int8_linear_backward_int8_workspace_bytes": (_sz, [_i64, _i64, _int]),
+    "int8_linear_backward_input_int8": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz,
+                                               _vp]),
 }
 
 
@@ -43,7 +46,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"HIP library not found at {LIB_PATH}; build it with "
-            "`python -m int8_quantized_linear_rowwise_amd.build` (hipcc, gfx950)")
+            "`python int8_quantized_linear_rowwise_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -1,6 +1,9 @@
 """Build the HIP library libint8lin.so in-tree for gfx950 (hipcc, no GPU needed).
 
-    python -m int8_quantized_linear_rowwise_amd.build [--jobs N]
+    python int8_quantized_linear_rowwise_amd/build.py [--jobs N]
+
+Run as a script (or load this file by path): importing the package itself
+loads the library and fails while it is missing or out of date.
 """
 from __future__ import annotations
 

@@ -169,4 +169,73 @@ int int8_linear_backward_input(const void* G, int dtype, int64_t M, int64_t N, c
   return I8L_OK;
 }
 
+// int8 backward workspace: count | SG (M fp32) | CG (M x N int8) | quantizer
+// scratch | grad_bias partial sums (when requested); 256-byte aligned blocks.
+struct Bwd8Layout {
+  size_t count, sg, cg, qs, gb, total;
+};
+
+static bool bwd8_layout(int64_t M, int64_t N, int with_grad_bias, Bwd8Layout* L) {
+  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX) return false;
+  size_t off = 0;
+  L->count = off;
+  off += ALIGN;
+  L->sg = off;
+  off += align_up((size_t)(M > 0 ? M : 1) * 4);
+  L->cg = off;
+  off += align_up((size_t)M * (size_t)N > 0 ? (size_t)M * (size_t)N : 1);
+  L->qs = off;
+  off += quant_scratch_bytes(M, N);
+  L->gb = off;
+  if (with_grad_bias) off += align_up(i8l::grad_bias_partial_floats((int)M, (int)N) * sizeof(float));
+  L->total = off;
+  return true;
+}
+
+size_t int8_linear_backward_int8_workspace_bytes(int64_t M, int64_t N, int with_grad_bias) {
+  Bwd8Layout L;
+  if (!bwd8_layout(M, N, with_grad_bias, &L)) return 0;
+  return L.total;
+}
+
+int int8_linear_backward_input_int8(const void* G, int dtype, int64_t M, int64_t N, const int8_t* CBt,
+                                    const float* SCBt, int64_t K, void* grad_A, void* grad_bias, int32_t* c32_debug,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return I8L_EDTYPE;
+  if (M < 0 || N < 0 || K < 0) return I8L_EINVAL;
+  if (M > INT32_MAX || K > INT32_MAX || N > I8L_MAX_K || N > I8L_MAX_COLS || M * K > ((int64_t)1 << 40) ||
+      M * N > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40))
+    return I8L_ESHAPE;
+  if (M > 0 && K > 0) {
+    if (grad_A == nullptr || SCBt == nullptr) return I8L_EINVAL;
+    if (N > 0 && (G == nullptr || CBt == nullptr)) return I8L_EINVAL;
+  }
+  if (grad_bias != nullptr && M > 0 && N > 0 && G == nullptr) return I8L_EINVAL;
+  Bwd8Layout L;
+  bwd8_layout(M, N, grad_bias != nullptr, &L);
+  if (ws == nullptr || ws_bytes < L.total) return I8L_EWORKSPACE;
+  if ((uintptr_t)ws % ALIGN) return I8L_EINVAL;
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = (hipStream_t)stream;
+  if (M > 0 && K > 0) {
+    int32_t* count = reinterpret_cast<int32_t*>(w + L.count);
+    float* SG = reinterpret_cast<float*>(w + L.sg);
+    int8_t* CG = reinterpret_cast<int8_t*>(w + L.cg);
+    uint32_t* qscratch = reinterpret_cast<uint32_t*>(w + L.qs);
+    // G row-wise with the split off (count 0), then the int8 product with the
+    // column-quantized weight copy: the forward kernel with K and N exchanged
+    hipError_t e = i8l::launch_quantize(dtype, G, M, (int)N, 0.0f, CG, SG, nullptr, count, nullptr, 0, qscratch, st);
+    if (e != hipSuccess) return I8L_EHIP;
+    e = i8l::launch_gemm_fwd(dtype, CG, SG, (int)M, CBt, SCBt, (int)K, (int)N, nullptr, 0, nullptr, count, nullptr,
+                             grad_A, c32_debug, st);
+    if (e != hipSuccess) return I8L_EHIP;
+  }
+  if (grad_bias != nullptr && N > 0) {
+    hipError_t e =
+        i8l::launch_grad_bias(dtype, G, (int)M, (int)N, reinterpret_cast<float*>(w + L.gb), grad_bias, st);
+    if (e != hipSuccess) return I8L_EHIP;
+  }
+  return I8L_OK;
+}
+
 }  // extern "C"

@@ -15,8 +15,12 @@ LIB = os.path.join(ROOT, "int8_quantized_linear_rowwise_amd", "libint8lin.so")
 @pytest.fixture(scope="module")
 def L():
     if not os.path.exists(LIB):
-        from int8_quantized_linear_rowwise_amd import build
-        build.build(verbose=False)
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_i8l_build", os.path.join(ROOT, "int8_quantized_linear_rowwise_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build(verbose=False)
     from int8_quantized_linear_rowwise_amd import _lib
     return _lib
 
@@ -140,6 +144,36 @@ def test_backward_host_errors(L):
     assert L.lib.int8_linear_backward_workspace_bytes(M, N, 0) == 0
 
 
+def test_backward_int8_host_errors(L):
+    f = L.lib.int8_linear_backward_input_int8
+    M, N, K = 8, 32, 64
+    ws = L.lib.int8_linear_backward_int8_workspace_bytes(M, N, 1)
+    assert ws >= M * N + 4 * M
+    base = dict(G=FAKE, dt=1, M=M, N=N, CB=FAKE, SCB=FAKE, K=K, gA=FAKE, gb=FAKE, c32=None, ws=FAKE, wsb=ws,
+                st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["G"], a["dt"], a["M"], a["N"], a["CB"], a["SCB"], a["K"], a["gA"], a["gb"], a["c32"], a["ws"],
+                 a["wsb"], a["st"])
+
+    assert call(dt=3) == L.I8L_EDTYPE
+    assert call(N=-1) == L.I8L_EINVAL
+    assert call(G=0) == L.I8L_EINVAL
+    assert call(CB=0) == L.I8L_EINVAL
+    assert call(SCB=0) == L.I8L_EINVAL
+    assert call(gA=0) == L.I8L_EINVAL
+    assert call(ws=0) == L.I8L_EWORKSPACE
+    assert call(wsb=ws - 1) == L.I8L_EWORKSPACE
+    assert call(ws=FAKE + 8) == L.I8L_EINVAL
+    # the contraction runs over the output features: the forward GEMM's limit applies to N
+    assert call(N=L.I8L_MAX_K + 1) == L.I8L_ESHAPE
+    assert call(M=1 << 32) == L.I8L_ESHAPE
+    assert (L.lib.int8_linear_backward_int8_workspace_bytes(M, N, 0)
+            < L.lib.int8_linear_backward_int8_workspace_bytes(M, N, 1))
+    assert L.lib.int8_linear_backward_int8_workspace_bytes(-1, N, 1) == 0
+
+
 def test_forward_layout(L):
     for (M, K, cap) in [(1, 1, 0), (600, 4, 4), (2048, 4096, 4096), (16384, 28672, 28672), (5, 70, 3)]:
         lay = L.ForwardLayout()
@@ -151,3 +185,28 @@ def test_forward_layout(L):
             assert o + s <= o2
         assert lay.total == L.lib.int8_linear_forward_workspace_bytes(M, K, cap)
     assert L.lib.int8_linear_forward_workspace_layout(-1, 4, 4, L.ForwardLayout()) == L.I8L_EINVAL
+
+
+def test_binding_rejects_mis_sized_results(L):
+    """Result tensors passed in by the caller are checked for shape and dtype
+    before any pointer reaches the library (a short buffer would be written
+    past its end by the kernels)."""
+    import torch
+    import int8_quantized_linear_rowwise_amd as I8
+    M, K, N = 4, 16, 8
+    A = torch.zeros((M, K), dtype=torch.float16)
+    G = torch.zeros((M, N), dtype=torch.float16)
+    CB, SCB = torch.zeros((N, K), dtype=torch.int8), torch.zeros(N)
+    CBt, SCBt = torch.zeros((K, N), dtype=torch.int8), torch.zeros(K)
+    bad = [
+        lambda: I8.int8_linear_forward(A, CB, SCB, out=torch.zeros((M, N - 1), dtype=torch.float16)),
+        lambda: I8.int8_linear_forward(A, CB, SCB, c32=torch.zeros((M, N), dtype=torch.float32)),
+        lambda: I8.int8_linear_backward_input(G, CB, SCB, grad_A=torch.zeros((M, K + 1), dtype=torch.float16)),
+        lambda: I8.int8_linear_backward_input(G, CB.float(), SCB),
+        lambda: I8.int8_linear_backward_input_int8(G, CBt, SCBt, c32=torch.zeros((M + 1, K), dtype=torch.int32)),
+        lambda: I8.int8_linear_backward_input_int8(G, CBt, SCBt, grad_bias=torch.zeros(N, dtype=torch.float32)),
+        lambda: I8.int8_linear_backward_input_int8(G, CB, SCB),
+    ]
+    for f in bad:
+        with pytest.raises(ValueError):
+            f()

@@ -162,7 +162,39 @@ def run_gpu(wl, steps, warmup, n_sets, threshold):
     q_ms = [sum(qev[rr][li][0].elapsed_time(qev[rr][li][1]) for rr in range(1, reps + 1)) / reps
             for li in range(nl)]
     del qbuf
-    return dict(layers=layers, gpu_ms=gpu_ms, host_s=h1 - h0, fwd_ms=fwd_ms, bwd_ms=bwd_ms, q_ms=q_ms)
+
+    # int8 backward variant (diagnostic, outside the timed region): G quantized
+    # row-wise times a second int8 weight copy quantized along the input
+    # features; the same rotation, every layer in reverse order, same stream
+    for ly in layers:
+        L = ly["L"]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234 + 101 * layers.index(ly))
+        W = torch.randn((L.N, L.K), generator=gen, device=dev, dtype=torch.float32) * wl.w_std
+        ly["CBt"], ly["SCBt"] = I8.quantize_weight_colwise(W)
+        ly["ws8"] = I8.backward_int8_workspace(L.M, L.N, ly["gb"] is not None, dev)
+        del W
+
+    def call_bwd8(ly, s):
+        _, G = ly["sets"][s]
+        I8.int8_linear_backward_input_int8(G, ly["CBt"], ly["SCBt"], with_grad_bias=ly["gb"] is not None,
+                                           grad_A=ly["gA"], grad_bias=ly["gb"], workspace=ly["ws8"])
+
+    for w in range(2):
+        for ly in reversed(layers):
+            call_bwd8(ly, w % n_sets)
+    b8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for k in range(steps):
+        b8[k][0].record(stream)
+        for ly in reversed(layers):
+            call_bwd8(ly, k % n_sets)
+        b8[k][1].record(stream)
+    torch.cuda.synchronize()
+    bwd8_ms = sum(a.elapsed_time(b) for a, b in b8) / steps
+    for ly in layers:
+        del ly["CBt"], ly["SCBt"], ly["ws8"]
+    return dict(layers=layers, gpu_ms=gpu_ms, host_s=h1 - h0, fwd_ms=fwd_ms, bwd_ms=bwd_ms, q_ms=q_ms,
+                bwd8_ms=bwd8_ms)
 
 
 def copy_calibration(nbytes=1 << 30):
@@ -307,6 +339,11 @@ def main():
                      "bwd_pct_fp16_peak": round(100 * bwd_tflops / PEAK_F16_TFLOPS, 2),
                      "quantizer_gbs_1read": round(q_gbs, 1),
                      "quantizer_pct_hbm": round(100 * q_gbs / PEAK_HBM_GBS, 2)},
+        "int8_backward": {"calls_ms": round(r["bwd8_ms"], 4),
+                          "int8_tops": round(bwd_flops / (r["bwd8_ms"] * 1e-3) / 1e12, 1),
+                          "step_tops_with_it": round(ops / ((fwd_ms + r["bwd8_ms"]) * 1e-3) / 1e12, 1),
+                          "note": "backward variant with G quantized to int8 (quantizer + int8 GEMM + grad_bias); "
+                                  "timed separately, not part of value"},
         "host_wall_s": round(r["host_s"], 3),
     }
     if not args.no_cpu_baseline:

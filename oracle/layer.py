@@ -51,6 +51,11 @@ Readings where the pages are silent (each also listed in the design notes):
      offline int8 copy, W^T (K x N) quantized by Q with the split off (one
      scale per input feature k); grad_A = D(C32 * SG[m] * SCBt[k] / 127^2)
      with C32 = CG . CBt^T exact; grad_bias as in reading 12.
+ 14. trainable-weight mode (BNB33 PR description: the has_fp16_weights option
+     beside the memory-efficient one; the pages give no formula): the weight
+     gradient of y = A16 W^T is grad_W[n, k] = D(sum_m G16[m, n] * A16[m, k]),
+     both operands cast to fp16 as in the rest of the layer (values beyond
+     fp16's range become +-inf), exact products, one rounding to D.
 
 Pins: tests/test_oracle_*.py (brute force with exact rationals, closed-form
 special cases, invariants, the pages' error bounds).
@@ -199,6 +204,20 @@ def linear_backward_input(G: np.ndarray, dt: str, CB: np.ndarray, SCB: np.ndarra
         g16 = to_half(G[idx[r0:r0 + chunk]], dt).astype(np.float64)
         ga[r0:r0 + chunk] = g16 @ W
     return {"y": ga, "grad_A": from_f64(ga, dt), "rows": idx}
+
+
+def linear_backward_weight(G: np.ndarray, A: np.ndarray, dt: str, rows=None) -> dict:
+    """Weight gradient of the trainable-weight mode (reading 14).
+
+    grad_W[n, k] = D(sum_m fp16(G[m, n]) * fp16(A[m, k])), the sum in float64
+    (products of fp16 values are exact there). ``rows`` restricts the output
+    to a subset of weight rows n.
+    """
+    idx = np.arange(G.shape[1]) if rows is None else np.asarray(rows)
+    g16 = to_half(G, dt)[:, idx].astype(np.float64)                     # M x |rows|
+    a16 = to_half(A, dt).astype(np.float64)                             # M x K
+    y = g16.T @ a16
+    return {"y": y, "grad_W": from_f64(y, dt), "rows": idx}
 
 
 def quantize_weight(W: np.ndarray, dt: str = "f32") -> tuple:

@@ -487,3 +487,70 @@ def test_mlp600_magnitude_against_printed_example():
     mine = oracle.page_bounds(r["out"], ref)
     assert mine["ok"], mine
     assert mine["max_rel"] < 5 * printed["max_rel"] + 0.02
+
+
+# --------------------------------------------------------------------------
+# weight gradient of the trainable-weight mode (oracle reading 14)
+
+
+def _exact_value(x, dt):
+    """Exact rational value of one stored element, decoded without the oracle's formats module."""
+    if dt == "bf16":
+        return Fraction(float(np.array([int(x) << 16], dtype=np.uint32).view(np.float32)[0]))
+    return Fraction(float(x))
+
+
+def test_wgrad_integer_case_is_textbook_matmul():
+    """Small integers are exact in fp16 and bf16, so grad_W = G^T A exactly
+    (non-square shapes: a transposed or swapped operand fails)."""
+    g = np.random.default_rng(70)
+    M, N, K = 37, 29, 23
+    G = g.integers(-100, 101, (M, N)).astype(np.float32)
+    A = g.integers(-100, 101, (M, K)).astype(np.float32)
+    ref = G.astype(np.int64).T @ A.astype(np.int64)
+    r = oracle.linear_backward_weight(G, A, "f32")
+    assert r["grad_W"].shape == (N, K)
+    assert np.array_equal(r["grad_W"], ref.astype(np.float32))
+    rb = oracle.linear_backward_weight(workloads._store(G, "bf16"), workloads._store(A, "bf16"), "bf16")
+    assert np.array_equal(rb["y"], ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_wgrad_brute_force(dt):
+    """Every element against the exact rational sum of exactly rounded fp16 casts."""
+    g = np.random.default_rng(71 + ["f16", "bf16", "f32"].index(dt))
+    for case in range(25):
+        M, N, K = int(g.integers(1, 7)), int(g.integers(1, 6)), int(g.integers(1, 6))
+        G = workloads._store((g.standard_normal((M, N)) * 0.01).astype(np.float32), dt)
+        A = workloads._store((g.standard_normal((M, K)) * 3).astype(np.float32), dt)
+        r = oracle.linear_backward_weight(G, A, dt)
+        g16 = [[exact_round(_exact_value(v, dt), "f16") for v in row] for row in G]
+        a16 = [[exact_round(_exact_value(v, dt), "f16") for v in row] for row in A]
+        for n in range(N):
+            for k in range(K):
+                y = sum((g16[m][n] * a16[m][k] for m in range(M)), Fraction(0))
+                assert abs(Fraction(float(r["y"][n, k])) - y) <= abs(y) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+                got = _exact_value(r["grad_W"][n, k], dt) if dt != "f32" else Fraction(float(r["grad_W"][n, k]))
+                assert got == exact_round(Fraction(float(r["y"][n, k])), dt)
+
+
+def test_wgrad_casts_operands_to_fp16():
+    """bf16 operands go through the fp16 cast: 3 * 2^-26 becomes the fp16
+    subnormal 2^-24, and 2^17 (beyond fp16's range) becomes inf."""
+    G = workloads._store(np.array([[3 * 2.0 ** -26, 1.0]], np.float32), "bf16")
+    A = workloads._store(np.array([[1.0, 2.0 ** 17]], np.float32), "bf16")
+    with np.errstate(over="ignore"):
+        r = oracle.linear_backward_weight(G, A, "bf16")
+    assert r["y"][0, 0] == 2.0 ** -24
+    assert np.isinf(r["y"][0, 1]) and np.isinf(r["y"][1, 1])
+    assert r["y"][1, 0] == 1.0
+
+
+def test_wgrad_rows_subset_matches_full():
+    g = np.random.default_rng(72)
+    G = workloads._store((g.standard_normal((50, 40)) * 0.01).astype(np.float32), "bf16")
+    A = workloads._store(g.standard_normal((50, 30)).astype(np.float32), "bf16")
+    full = oracle.linear_backward_weight(G, A, "bf16")
+    rows = np.array([7, 0, 39])
+    part = oracle.linear_backward_weight(G, A, "bf16", rows=rows)
+    assert np.array_equal(part["grad_W"], full["grad_W"][rows])

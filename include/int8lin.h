@@ -167,6 +167,20 @@ int int8_linear_backward_input_int8(const void* G, int dtype, int64_t M, int64_t
                                     const float* SCBt, int64_t K, void* grad_A, void* grad_bias, int32_t* c32_debug,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * Weight gradient of the trainable-weight mode (bitsandbytes PR #33 names a
+ * has_fp16_weights option beside the memory-efficient backward; the weight
+ * then stays a trainable tensor that is re-quantized on each forward):
+ *   grad_W[n, k] = D(sum_m fp16(G[m, n]) * fp16(A[m, k]))   (fp32 accumulate)
+ * G: M x N and A: M x K of `dtype` (the output gradient and the layer input,
+ * both row-major); grad_W: N x K of `dtype`, row-major (the weight's layout).
+ * M = 0 writes zeros. Needs no workspace. Errors: I8L_EDTYPE, I8L_EINVAL
+ * (negative size, NULL pointer where data is needed), I8L_ESHAPE (a size
+ * beyond INT32_MAX or a product beyond 2^40), I8L_EHIP (launch failure).
+ * ------------------------------------------------------------------------ */
+int int8_linear_backward_weight(const void* G, const void* A, int dtype, int64_t M, int64_t N, int64_t K,
+                                void* grad_W, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

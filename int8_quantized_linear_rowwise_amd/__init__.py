@@ -24,6 +24,7 @@ from ._lib import (I8L_BF16, I8L_F16, I8L_F32, I8L_MAX_K, Int8LinError, check, l
 __all__ = [
     "int8_quantize_rowwise", "int8_linear_forward", "int8_linear_backward_input", "quantize_weight",
     "quantize_weight_colwise", "int8_linear_backward_input_int8", "backward_int8_workspace",
+    "int8_linear_backward_weight",
     "Int8LinearFunction", "Int8Linear", "Int8LinError", "forward_workspace", "forward_layout",
     "forward_check", "DTYPE_CODE", "I8L_MAX_K",
 ]
@@ -229,6 +230,25 @@ def int8_linear_backward_input_int8(G: torch.Tensor, CBt: torch.Tensor, SCBt: to
                                               _stream(G.device)),
           "int8_linear_backward_input_int8")
     return grad_A, grad_bias
+
+
+def int8_linear_backward_weight(G: torch.Tensor, A: torch.Tensor, grad_W: Optional[torch.Tensor] = None):
+    """Weight gradient of the trainable-weight mode: grad_W = D(fp16(G)^T @ fp16(A)), fp32 accumulation.
+
+    G: M x N output gradient; A: M x K layer input (same dtype); returns N x K in that dtype."""
+    if G.dim() != 2 or A.dim() != 2 or G.shape[0] != A.shape[0]:
+        raise ValueError("G (M x N) and A (M x K) must be 2-D with the same number of rows")
+    if G.dtype != A.dtype:
+        raise ValueError("G and A must have the same dtype")
+    M, N = G.shape
+    K = A.shape[1]
+    _check_out(grad_W, (N, K), G.dtype, "grad_W")
+    if grad_W is None:
+        grad_W = _empty((N, K), G.dtype, G.device)
+    check(lib.int8_linear_backward_weight(_dev(G, "G"), _dev(A, "A"), _code(G), M, N, K, _dev(grad_W, "grad_W"),
+                                          _stream(G.device)),
+          "int8_linear_backward_weight")
+    return grad_W
 
 
 # ----------------------------------------------------------------------------

@@ -39,6 +39,7 @@ SIGNATURES = {
     "int8_linear_backward_int8_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "int8_linear_backward_input_int8": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz,
                                                _vp]),
+    "int8_linear_backward_weight": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _vp, _vp]),
 }
 
 

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libint8lin.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "quantize.hip", "gemm_fwd.hip", "gemm_bwd.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm_fwd.hip", "gemm_bwd.hip", "gemm_wgrad.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("I8L_OFFLOAD_ARCH", "gfx950")

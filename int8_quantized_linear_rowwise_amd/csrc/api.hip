@@ -238,4 +238,17 @@ int int8_linear_backward_input_int8(const void* G, int dtype, int64_t M, int64_t
   return I8L_OK;
 }
 
+int int8_linear_backward_weight(const void* G, const void* A, int dtype, int64_t M, int64_t N, int64_t K,
+                                void* grad_W, void* stream) {
+  if (!valid_dtype(dtype)) return I8L_EDTYPE;
+  if (M < 0 || N < 0 || K < 0) return I8L_EINVAL;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || M * K > ((int64_t)1 << 40) ||
+      M * N > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40))
+    return I8L_ESHAPE;
+  if (N == 0 || K == 0) return I8L_OK;
+  if (grad_W == nullptr) return I8L_EINVAL;
+  if (M > 0 && (G == nullptr || A == nullptr)) return I8L_EINVAL;
+  return hip_status(i8l::launch_gemm_wgrad(dtype, G, A, (int)M, (int)N, (int)K, grad_W, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -24,6 +24,10 @@ hipError_t launch_gemm_fwd(int dt, const int8_t* CA, const float* SCA, int M, co
 hipError_t launch_gemm_bwd(int dt, const void* G, int M, int N, const int8_t* CB, const float* SCB, int K,
                            void* grad_A, hipStream_t st);
 
+// Weight gradient of the trainable-weight mode: grad_W = D(fp16(G)^T . fp16(A)).
+hipError_t launch_gemm_wgrad(int dt, const void* G, const void* A, int M, int N, int K, void* grad_W,
+                             hipStream_t st);
+
 // grad_bias[n] = D(sum_m G[m, n]) (fp32 accumulation, fixed order).
 size_t grad_bias_partial_floats(int M, int N);
 hipError_t launch_grad_bias(int dt, const void* G, int M, int N, float* partial, void* grad_bias, hipStream_t st);

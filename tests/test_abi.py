@@ -174,6 +174,26 @@ def test_backward_int8_host_errors(L):
     assert L.lib.int8_linear_backward_int8_workspace_bytes(-1, N, 1) == 0
 
 
+def test_backward_weight_host_errors(L):
+    f = L.lib.int8_linear_backward_weight
+    base = dict(G=FAKE, A=FAKE, dt=2, M=64, N=32, K=16, gW=FAKE, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["G"], a["A"], a["dt"], a["M"], a["N"], a["K"], a["gW"], a["st"])
+
+    assert call(dt=7) == L.I8L_EDTYPE
+    assert call(M=-1) == L.I8L_EINVAL
+    assert call(G=0) == L.I8L_EINVAL
+    assert call(A=0) == L.I8L_EINVAL
+    assert call(gW=0) == L.I8L_EINVAL
+    assert call(N=1 << 31) == L.I8L_ESHAPE
+    assert call(M=1 << 21, N=1 << 20) == L.I8L_ESHAPE
+    # nothing to write: no pointer is needed and nothing is launched
+    assert call(N=0, G=0, A=0, gW=0) == L.I8L_OK
+    assert call(K=0, G=0, A=0, gW=0) == L.I8L_OK
+
+
 def test_forward_layout(L):
     for (M, K, cap) in [(1, 1, 0), (600, 4, 4), (2048, 4096, 4096), (16384, 28672, 28672), (5, 70, 3)]:
         lay = L.ForwardLayout()
@@ -206,6 +226,9 @@ def test_binding_rejects_mis_sized_results(L):
         lambda: I8.int8_linear_backward_input_int8(G, CBt, SCBt, c32=torch.zeros((M + 1, K), dtype=torch.int32)),
         lambda: I8.int8_linear_backward_input_int8(G, CBt, SCBt, grad_bias=torch.zeros(N, dtype=torch.float32)),
         lambda: I8.int8_linear_backward_input_int8(G, CB, SCB),
+        lambda: I8.int8_linear_backward_weight(G, A, grad_W=torch.zeros((K, N), dtype=torch.float16)),
+        lambda: I8.int8_linear_backward_weight(G, A[:3]),
+        lambda: I8.int8_linear_backward_weight(G, A.float()),
     ]
     for f in bad:
         with pytest.raises(ValueError):

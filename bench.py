@@ -193,8 +193,32 @@ def run_gpu(wl, steps, warmup, n_sets, threshold):
     bwd8_ms = sum(a.elapsed_time(b) for a, b in b8) / steps
     for ly in layers:
         del ly["CBt"], ly["SCBt"], ly["ws8"]
+
+    # weight gradient of the trainable-weight mode (diagnostic, outside the
+    # timed region): every layer in reverse order, same rotation and stream
+    for ly in layers:
+        L = ly["L"]
+        ly["gW"] = torch.empty((L.N, L.K), dtype=ly["gA"].dtype, device=dev)
+
+    def call_wgrad(ly, s):
+        A, G = ly["sets"][s]
+        I8.int8_linear_backward_weight(G, A, grad_W=ly["gW"])
+
+    for w in range(2):
+        for ly in reversed(layers):
+            call_wgrad(ly, w % n_sets)
+    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for k in range(steps):
+        wev[k][0].record(stream)
+        for ly in reversed(layers):
+            call_wgrad(ly, k % n_sets)
+        wev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wgrad_ms = sum(a.elapsed_time(b) for a, b in wev) / steps
+    for ly in layers:
+        del ly["gW"]
     return dict(layers=layers, gpu_ms=gpu_ms, host_s=h1 - h0, fwd_ms=fwd_ms, bwd_ms=bwd_ms, q_ms=q_ms,
-                bwd8_ms=bwd8_ms)
+                bwd8_ms=bwd8_ms, wgrad_ms=wgrad_ms)
 
 
 def copy_calibration(nbytes=1 << 30):
@@ -344,6 +368,11 @@ def main():
                           "step_tops_with_it": round(ops / ((fwd_ms + r["bwd8_ms"]) * 1e-3) / 1e12, 1),
                           "note": "backward variant with G quantized to int8 (quantizer + int8 GEMM + grad_bias); "
                                   "timed separately, not part of value"},
+        "weight_grad": {"calls_ms": round(r["wgrad_ms"], 4),
+                        "fp16_tflops": round(bwd_flops / (r["wgrad_ms"] * 1e-3) / 1e12, 1),
+                        "pct_fp16_peak": round(100 * bwd_flops / (r["wgrad_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
+                        "note": "trainable-weight mode's grad_W = fp16(G)^T fp16(A) of every layer; timed "
+                                "separately, not part of value"},
         "host_wall_s": round(r["host_s"], 3),
     }
     if not args.no_cpu_baseline:

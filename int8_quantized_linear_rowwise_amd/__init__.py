@@ -24,7 +24,7 @@ from ._lib import (I8L_BF16, I8L_F16, I8L_F32, I8L_MAX_K, Int8LinError, check, l
 __all__ = [
     "int8_quantize_rowwise", "int8_linear_forward", "int8_linear_backward_input", "quantize_weight",
     "quantize_weight_colwise", "int8_linear_backward_input_int8", "backward_int8_workspace",
-    "int8_linear_backward_weight",
+    "int8_linear_backward_weight", "Int8LinearTrainableFunction", "Int8LinearTrainable",
     "Int8LinearFunction", "Int8Linear", "Int8LinError", "forward_workspace", "forward_layout",
     "forward_check", "DTYPE_CODE", "I8L_MAX_K",
 ]
@@ -287,6 +287,39 @@ class Int8LinearFunction(torch.autograd.Function):
         return gA, None, None, gb, None
 
 
+class Int8LinearTrainableFunction(torch.autograd.Function):
+    """Trainable-weight mode (bitsandbytes' has_fp16_weights option): the weight W
+    (same dtype as the input) is quantized on each forward; the backward returns
+    grad_A through the memory-efficient kernel from this call's int8 weights and
+    grad_W = D(fp16(G)^T fp16(A))."""
+
+    @staticmethod
+    def forward(ctx, A, W, bias, threshold):
+        if W.dtype != A.dtype:
+            raise ValueError("the trainable weight must have the input's dtype")
+        shape = A.shape
+        A2 = A.reshape(-1, shape[-1]).contiguous()
+        CB, SCB = quantize_weight(W.detach().contiguous())
+        out = int8_linear_forward(A2, CB, SCB, bias, threshold)
+        ctx.save_for_backward(A2, CB, SCB)
+        ctx.grad_shape = shape
+        ctx.has_bias = bias is not None
+        return out.reshape(*shape[:-1], CB.shape[0])
+
+    @staticmethod
+    def backward(ctx, g):
+        A2, CB, SCB = ctx.saved_tensors
+        g2 = g.reshape(-1, g.shape[-1]).contiguous()
+        need_b = ctx.has_bias and ctx.needs_input_grad[2]
+        gA = gb = gW = None
+        if ctx.needs_input_grad[0] or need_b:
+            gA, gb = int8_linear_backward_input(g2, CB, SCB, with_grad_bias=need_b)
+            gA = gA.reshape(ctx.grad_shape) if ctx.needs_input_grad[0] else None
+        if ctx.needs_input_grad[1]:
+            gW = int8_linear_backward_weight(g2, A2)
+        return gA, gW, gb, None
+
+
 class Int8Linear(torch.nn.Module):
     """Linear layer with int8 row-major weights (quantized once) and a trainable bias."""
 
@@ -301,3 +334,17 @@ class Int8Linear(torch.nn.Module):
     def forward(self, x):
         b = self.bias.to(x.dtype) if self.bias is not None else None
         return Int8LinearFunction.apply(x, self.CB, self.SCB, b, self.threshold)
+
+
+class Int8LinearTrainable(torch.nn.Module):
+    """Linear layer in the trainable-weight mode: W is a parameter (kept in the
+    input dtype) that is re-quantized to int8 on every forward."""
+
+    def __init__(self, weight: torch.Tensor, bias: Optional[torch.Tensor] = None, threshold: float = 6.0):
+        super().__init__()
+        self.weight = torch.nn.Parameter(weight.detach().clone())
+        self.bias = torch.nn.Parameter(bias.detach().clone()) if bias is not None else None
+        self.threshold = float(threshold)
+
+    def forward(self, x):
+        return Int8LinearTrainableFunction.apply(x, self.weight, self.bias, self.threshold)

@@ -134,3 +134,32 @@ def test_wgrad_full_size_block(I8):
     r = oracle.linear_backward_weight(G, A, wl.dtype, rows=rows)
     assert_accum_gate(host(gW.index_select(0, torch.from_numpy(rows).to("cuda:0"))), wl.dtype, r["y"], G, A,
                       rows, "grad_W (sampled rows)")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_trainable_module_matches_c_calls(I8, dt):
+    """The trainable-weight module: output and all three gradients equal the
+    C calls bit for bit, and after an update the forward uses the re-quantized
+    weight."""
+    M, K, N = 96, 264, 80
+    c = workloads.small_case(dt, M, K, N, 34, n_outliers=3, has_bias=True)
+    A, W, b, G = c["A"], workloads._store(c["W"], dt), c["bias"], c["G"]
+    lin = I8.Int8LinearTrainable(dev(W, dt), dev(b, dt))
+    x = dev(A, dt).reshape(2, 48, K).requires_grad_(True)
+    y = lin(x)
+    y.backward(dev(G, dt).reshape(2, 48, N))
+    CB, SCB = I8.quantize_weight(dev(W, dt))
+    out = I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt), 6.0)
+    gA, gb = I8.int8_linear_backward_input(dev(G, dt), CB, SCB)
+    gW = I8.int8_linear_backward_weight(dev(G, dt), dev(A, dt))
+    assert_bits_equal(host(y.detach().reshape(M, N)), host(out), "module out")
+    assert_bits_equal(host(x.grad.reshape(M, K)), host(gA), "module grad_A")
+    assert_bits_equal(host(lin.weight.grad), host(gW), "module grad_W")
+    assert_bits_equal(host(lin.bias.grad), host(gb), "module grad_bias")
+    with torch.no_grad():
+        lin.weight -= 0.5 * lin.weight.grad
+    y2 = lin(dev(A, dt))
+    CB2, SCB2 = I8.quantize_weight(lin.weight.detach())
+    assert not torch.equal(CB2, CB)
+    assert_bits_equal(host(y2.detach()), host(I8.int8_linear_forward(dev(A, dt), CB2, SCB2, dev(b, dt), 6.0)),
+                      "forward after the update")

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace i8l {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -187,6 +189,19 @@ __device__ __forceinline__ void otile_store(const char* ot, T* __restrict__ dst,
         if (c + e < C) p[e] = __builtin_bit_cast(T, (uint16_t)(v[e >> 1] >> (16 * (e & 1))));
     }
   }
+}
+
+// Raises a kernel's dynamic-LDS limit once per device (the attribute is per
+// device; the bit mask remembers devices 0..63 already set up).
+inline hipError_t lds_limit_once(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 // Wave-wide reductions (wave64).

@@ -679,11 +679,10 @@ static hipError_t launch_bwd_w8(const void* G, int M, int N, const int8_t* CB, c
   typedef typename Elem<DT>::T T;
   constexpr size_t lds = (size_t)2 * (256 + 256) * 128;
   auto kern = k_gemm_bwd_w8<DT, OV>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int tiles = ((M + 255) / 256) * ((K + 255) / 256);
   hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), lds, st, static_cast<const T*>(G), M, N, CB, SCB, K,
@@ -697,11 +696,10 @@ static hipError_t launch_bwd_big(const void* G, int M, int N, const int8_t* CB, 
   typedef typename Elem<DT>::T T;
   constexpr size_t lds = (size_t)2 * (256 + 256) * 128;
   auto kern = k_gemm_bwd_big<DT, OV>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int tiles = ((M + 255) / 256) * ((K + 255) / 256);
   hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, static_cast<const T*>(G), M, N, CB, SCB, K,
@@ -716,11 +714,10 @@ static hipError_t launch_bwd_cfg(const void* G, int M, int N, const int8_t* CB, 
   constexpr int LDN = BNC + 8;
   constexpr size_t lds = (size_t)2 * (BK + BM) * LDN * sizeof(_Float16);
   auto kern = k_gemm_bwd<BM, BK, BNC, DT, GV, WV, OV>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int tiles = ((M + BM - 1) / BM) * ((K + BK - 1) / BK);
   hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, static_cast<const T*>(G), M, N, CB, SCB, K,

@@ -701,11 +701,10 @@ static hipError_t launch_fwd_w8(const int8_t* CA, const float* SCA, int M, const
   typedef typename Elem<DT>::T T;
   constexpr size_t lds = (size_t)2 * (256 + 256) * 128 + OPAN_BYTES + LSC_BYTES;   // stages, panels, scales
   auto kern = k_gemm_fwd_w8<DT, OV>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
   hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count,
@@ -721,11 +720,10 @@ static hipError_t launch_fwd_cfg(const int8_t* CA, const float* SCA, int M, cons
   constexpr int LDK = BK + 16;
   constexpr size_t lds = (size_t)2 * (BM + BN) * LDK;
   auto kern = k_gemm_fwd<BM, BN, BK, DT, KV, OV>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count,
@@ -740,11 +738,10 @@ static hipError_t launch_fwd_big(const int8_t* CA, const float* SCA, int M, cons
   typedef typename Elem<DT>::T T;
   constexpr size_t lds = (size_t)2 * (256 + 256) * 128;
   auto kern = k_gemm_fwd_big<DT, OV>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
   hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count,

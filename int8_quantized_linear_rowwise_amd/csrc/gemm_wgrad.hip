@@ -235,11 +235,10 @@ static hipError_t launch_wgrad_big(const void* G, const void* A, int M, int N, i
   typedef typename Elem<DT>::T T;
   constexpr size_t lds = (size_t)2 * 2 * 64 * 512;   // also holds the 256 x 512-byte output tile
   auto kern = k_gemm_wgrad<DT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int tiles = ((N + 255) / 256) * ((K + 255) / 256);
   hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), lds, st, static_cast<const T*>(G), static_cast<const T*>(A), M, N,

@@ -15,6 +15,10 @@
  *   - author notes: grad_bias from the un-cast gradient; frozen weight (no
  *     weight gradient).
  *   - review on the backward dequantization: CB * (SCB * (1/127)).
+ *   - the has_fp16_weights option beside the memory-efficient one (a trainable
+ *     weight re-quantized on each forward): int8_linear_backward_weight.
+ * and EasyDeL discussion #66 ("Run and find Out": fwd_bits=8, bwd_bits=8), an
+ * 8-bit backward dot product: int8_linear_backward_input_int8.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller (the library

@@ -15,13 +15,13 @@ from .formats import (bf16_bits_to_f64, f64_to_bf16_bits, from_f64, round_to_for
                       to_half, ulp)
 from .layer import (dequant_weight, grad_bias, int_matmul, linear_backward_input,
                     linear_backward_input_int8, linear_backward_weight, linear_forward, mlp_forward_backward, outlier_columns,
-                    page_bounds, quantize_rowwise, quantize_weight, quantize_weight_colwise, silu,
+                    page_bounds, quantize_rowwise, quantize_weight, quantize_weight_colwise, silu, silu_activation,
                     silu_grad, threshold_active)
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "from_f64", "round_to_format", "to_f64", "to_half",
     "ulp", "dequant_weight", "grad_bias", "int_matmul", "linear_backward_input",
     "linear_backward_input_int8", "linear_backward_weight", "linear_forward", "mlp_forward_backward", "outlier_columns",
-    "page_bounds", "quantize_rowwise", "quantize_weight", "quantize_weight_colwise", "silu",
+    "page_bounds", "quantize_rowwise", "quantize_weight", "quantize_weight_colwise", "silu", "silu_activation",
     "silu_grad", "threshold_active",
 ]

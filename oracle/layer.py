@@ -56,6 +56,11 @@ Readings where the pages are silent (each also listed in the design notes):
      gradient of y = A16 W^T is grad_W[n, k] = D(sum_m G16[m, n] * A16[m, k]),
      both operands cast to fp16 as in the rest of the layer (values beyond
      fp16's range become +-inf), exact products, one rounding to D.
+ 15. producer-side outlier flags (EasyDeL discussion #66's MLP: Dense -> SiLU
+     -> Dense): the SiLU between the linears is applied to the first
+     linear's output as stored in D and rounded to D once; the kernel that
+     produces A = D(SiLU(H)) may also hand over A's outlier columns, which
+     are by definition those the quantizer would find in A (readings 1-3, 7).
 
 Pins: tests/test_oracle_*.py (brute force with exact rationals, closed-form
 special cases, invariants, the pages' error bounds).
@@ -255,6 +260,16 @@ def linear_backward_input_int8(G: np.ndarray, dt: str, CBt: np.ndarray, SCBt: np
 
 def silu(h: np.ndarray) -> np.ndarray:
     return h / (1.0 + np.exp(-h))
+
+
+def silu_activation(H: np.ndarray, dt: str) -> dict:
+    """The activation between the two linears of EasyDeL discussion #66's
+    "Run and find Out" MLP, applied to the first linear's output H as stored
+    in D: A = D(SiLU(H)), SiLU in float64 and one rounding (reading 15). The
+    outlier columns of A (the second linear's input) are
+    outlier_columns(fp16(A), tau), as the quantizer finds them."""
+    y = silu(to_f64(H, dt))
+    return {"y": y, "A": from_f64(y, dt)}
 
 
 def silu_grad(h: np.ndarray) -> np.ndarray:

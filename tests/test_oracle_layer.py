@@ -554,3 +554,33 @@ def test_wgrad_rows_subset_matches_full():
     rows = np.array([7, 0, 39])
     part = oracle.linear_backward_weight(G, A, "bf16", rows=rows)
     assert np.array_equal(part["grad_W"], full["grad_W"][rows])
+
+
+# --------------------------------------------------------------------------
+# SiLU between the EasyDeL MLP's linears, with producer-side outlier flags (reading 15)
+
+
+def test_silu_closed_forms():
+    """SiLU(x) - SiLU(-x) = x for every x (x s(x) + x s(-x) = x), SiLU(0) = 0,
+    SiLU(x) -> x and SiLU(-x) -> 0 for large x, and the well-known minimum
+    near x = -1.2785 of about -0.2785 (the root of 1 + x (1 - s(x)) = 0)."""
+    x = np.linspace(-30, 30, 6001)
+    assert np.allclose(oracle.silu(x) - oracle.silu(-x), x, rtol=0, atol=1e-12)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(oracle.silu(np.array([-40.0]))[0]) < 1e-15
+    xm = x[np.argmin(oracle.silu(x))]
+    assert abs(xm + 1.2785) < 0.01 and abs(oracle.silu(np.array([xm]))[0] + 0.2785) < 1e-3
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_silu_activation_rounds_once(dt):
+    g = np.random.default_rng(90)
+    H = workloads._store((g.standard_normal((40, 30)) * 4).astype(np.float32), dt)
+    r = oracle.silu_activation(H, dt)
+    h = to_f64(H, dt)
+    assert np.array_equal(r["y"], h / (1.0 + np.exp(-h)))
+    # one rounding: A is the stored value nearest to y
+    a = to_f64(r["A"], dt)
+    u = oracle.ulp(np.abs(r["y"]), dt)
+    assert np.all(np.abs(a - r["y"]) <= 0.5 * u + 1e-300)

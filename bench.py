@@ -217,8 +217,43 @@ def run_gpu(wl, steps, warmup, n_sets, threshold):
     wgrad_ms = sum(a.elapsed_time(b) for a, b in wev) / steps
     for ly in layers:
         del ly["gW"]
+
+    # producer-side outlier flags (diagnostic): for the layer with the widest
+    # input, its input made by the SiLU kernel from a same-shaped tensor, then
+    # the forward with its own flagging pass against the flagged forward
+    ly = max(layers, key=lambda l: l["L"].K)
+    L = ly["L"]
+    Hs = [ly["sets"][s][0] for s in range(n_sets)]
+    As = [torch.empty_like(h) for h in Hs]
+    fls = [I8.outlier_flags_buffer(L.M, L.K, dev) for _ in Hs]
+
+    def silu_leg(s):
+        I8.silu_outlier_flags(Hs[s], threshold, A=As[s], flags=fls[s])
+
+    def fwd_plain(s):
+        I8.int8_linear_forward(As[s], ly["CB"], ly["SCB"], ly["bias"], threshold, L.K, out=ly["out"],
+                               workspace=ly["wsf"])
+
+    def fwd_flagged(s):
+        I8.int8_linear_forward_flagged(As[s], fls[s], ly["CB"], ly["SCB"], ly["bias"], L.K, out=ly["out"],
+                                       workspace=ly["wsf"])
+
+    def timed_leg(f, reps=10):
+        for w in range(2):
+            f(w % n_sets)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for k in range(reps):
+            evs[k][0].record(stream)
+            f(k % n_sets)
+            evs[k][1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
+
+    pf = dict(layer=f"{L.name} {L.M}x{L.K}", silu_flags_ms=timed_leg(silu_leg), forward_ms=timed_leg(fwd_plain),
+              forward_flagged_ms=timed_leg(fwd_flagged))
+    del As, fls
     return dict(layers=layers, gpu_ms=gpu_ms, host_s=h1 - h0, fwd_ms=fwd_ms, bwd_ms=bwd_ms, q_ms=q_ms,
-                bwd8_ms=bwd8_ms, wgrad_ms=wgrad_ms)
+                bwd8_ms=bwd8_ms, wgrad_ms=wgrad_ms, pf=pf)
 
 
 def copy_calibration(nbytes=1 << 30):
@@ -373,6 +408,12 @@ def main():
                         "pct_fp16_peak": round(100 * bwd_flops / (r["wgrad_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
                         "note": "trainable-weight mode's grad_W = fp16(G)^T fp16(A) of every layer; timed "
                                 "separately, not part of value"},
+        "producer_flags": {"layer": r["pf"]["layer"], "silu_and_flags_ms": round(r["pf"]["silu_flags_ms"], 4),
+                           "forward_ms": round(r["pf"]["forward_ms"], 4),
+                           "forward_with_producer_flags_ms": round(r["pf"]["forward_flagged_ms"], 4),
+                           "note": "the widest-input layer's forward with its own flagging pass, and with the "
+                                   "flags the SiLU kernel made while producing its input (median of 10 calls); "
+                                   "not part of value"},
         "host_wall_s": round(r["host_s"], 3),
     }
     if not args.no_cpu_baseline:

@@ -25,6 +25,7 @@ __all__ = [
     "int8_quantize_rowwise", "int8_linear_forward", "int8_linear_backward_input", "quantize_weight",
     "quantize_weight_colwise", "int8_linear_backward_input_int8", "backward_int8_workspace",
     "int8_linear_backward_weight", "Int8LinearTrainableFunction", "Int8LinearTrainable",
+    "outlier_flags_buffer", "silu_outlier_flags", "int8_linear_forward_flagged",
     "Int8LinearFunction", "Int8Linear", "Int8LinError", "forward_workspace", "forward_layout",
     "forward_check", "DTYPE_CODE", "I8L_MAX_K",
 ]
@@ -158,6 +159,63 @@ def int8_linear_forward(A: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor, bi
                                   _dev(bias, "bias"), float(threshold), cap, _dev(out, "out"), _dev(c32, "c32"),
                                   workspace.data_ptr(), workspace.numel(), _stream(A.device)),
           "int8_linear_forward")
+    return out
+
+
+def outlier_flags_buffer(rows: int, cols: int, device) -> torch.Tensor:
+    """A flag buffer for an input of rows x cols (int32 words)."""
+    n = lib.int8_outlier_flags_words(rows, cols)
+    return _empty((max(n, 1),), torch.int32, device)
+
+
+def silu_outlier_flags(H: torch.Tensor, threshold: float = 6.0, A: Optional[torch.Tensor] = None,
+                       flags: Optional[torch.Tensor] = None):
+    """A = SiLU(H) in H's dtype and A's outlier-column flags for `threshold`, in one pass
+    (the activation between two int8 linears, producing the second one's input)."""
+    if H.dim() != 2:
+        raise ValueError("H must be 2-D (flatten leading dimensions)")
+    R, C = H.shape
+    _check_out(A, (R, C), H.dtype, "A")
+    if A is None:
+        A = _empty((R, C), H.dtype, H.device)
+    n = lib.int8_outlier_flags_words(R, C)
+    if flags is None:
+        flags = outlier_flags_buffer(R, C, H.device)
+    elif flags.dtype != torch.int32 or flags.numel() < n:
+        raise ValueError(f"flags must be int32 with at least {n} elements")
+    check(lib.int8_silu_outlier_flags(_dev(H, "H"), _code(H), R, C, float(threshold), _dev(A, "A"),
+                                      _dev(flags, "flags"), _stream(H.device)),
+          "int8_silu_outlier_flags")
+    return A, flags
+
+
+def int8_linear_forward_flagged(A: torch.Tensor, flags: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,
+                                bias: Optional[torch.Tensor] = None, cap: Optional[int] = None,
+                                out: Optional[torch.Tensor] = None, c32: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None):
+    """int8_linear_forward with the outlier columns taken from `flags` (from silu_outlier_flags on A's shape)."""
+    if A.dim() != 2 or CB.dim() != 2:
+        raise ValueError("A and CB must be 2-D")
+    M, K = A.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or SCB.shape != (N,) or CB.dtype != torch.int8 or SCB.dtype != torch.float32:
+        raise ValueError("CB must be N x K int8 and SCB N fp32")
+    if bias is not None and (bias.shape != (N,) or bias.dtype != A.dtype):
+        raise ValueError("bias must have shape (N,) and A's dtype")
+    if flags.dtype != torch.int32 or flags.numel() < lib.int8_outlier_flags_words(M, K):
+        raise ValueError("flags must be the int32 flag buffer of an M x K input")
+    cap = K if cap is None else int(cap)
+    _check_out(out, (M, N), A.dtype, "out")
+    _check_out(c32, (M, N), torch.int32, "c32")
+    if out is None:
+        out = _empty((M, N), A.dtype, A.device)
+    if workspace is None:
+        workspace = forward_workspace(M, K, cap, A.device)
+    check(lib.int8_linear_forward_flagged(_dev(A, "A"), _code(A), M, K, _dev(flags, "flags"), _dev(CB, "CB"),
+                                          _dev(SCB, "SCB"), N, _dev(bias, "bias"), cap, _dev(out, "out"),
+                                          _dev(c32, "c32"), workspace.data_ptr(), workspace.numel(),
+                                          _stream(A.device)),
+          "int8_linear_forward_flagged")
     return out
 
 

@@ -89,9 +89,9 @@ int int8_linear_forward_workspace_layout(int64_t M, int64_t K, int32_t cap, i8l_
   return I8L_OK;
 }
 
-int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
-                        int64_t N, const void* bias, float threshold, int32_t cap, void* out, int32_t* c32,
-                        void* ws, size_t ws_bytes, void* stream) {
+static int forward_impl(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
+                        int64_t N, const void* bias, float threshold, const uint32_t* preflags, int32_t cap,
+                        void* out, int32_t* c32, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dtype)) return I8L_EDTYPE;
   if (M < 0 || K < 0 || N < 0 || cap < 0) return I8L_EINVAL;
   if (M > INT32_MAX || N > INT32_MAX || K > I8L_MAX_K || M * K > ((int64_t)1 << 40) ||
@@ -114,11 +114,40 @@ int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const in
   uint16_t* subA = reinterpret_cast<uint16_t*>(w + L.sub);
   uint32_t* qscratch = reinterpret_cast<uint32_t*>(w + L.total - quant_scratch_bytes(M, K));
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = i8l::launch_quantize(dtype, A, M, (int)K, threshold, CA, SCA, idx, count, subA, cap, qscratch, st);
+  hipError_t e = i8l::launch_quantize(dtype, A, M, (int)K, threshold, CA, SCA, idx, count, subA, cap, qscratch, st,
+                                      preflags);
   if (e != hipSuccess) return I8L_EHIP;
   e = i8l::launch_gemm_fwd(dtype, CA, SCA, (int)M, CB, SCB, (int)N, (int)K, subA, cap, idx, count, bias, out, c32,
                            st);
   return hip_status(e);
+}
+
+int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
+                        int64_t N, const void* bias, float threshold, int32_t cap, void* out, int32_t* c32,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(A, dtype, M, K, CB, SCB, N, bias, threshold, nullptr, cap, out, c32, ws, ws_bytes, stream);
+}
+
+size_t int8_outlier_flags_words(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return i8l::quant_scratch_words(rows, cols);
+}
+
+int int8_silu_outlier_flags(const void* H, int dtype, int64_t rows, int64_t cols, float threshold, void* A,
+                            uint32_t* flags, void* stream) {
+  if (!valid_dtype(dtype)) return I8L_EDTYPE;
+  if (rows < 0 || cols < 0) return I8L_EINVAL;
+  if (rows > INT32_MAX || cols > I8L_MAX_COLS || rows * cols > ((int64_t)1 << 40)) return I8L_ESHAPE;
+  if (rows == 0 || cols == 0) return I8L_OK;
+  if (H == nullptr || A == nullptr || flags == nullptr) return I8L_EINVAL;
+  return hip_status(i8l::launch_silu_flags(dtype, H, rows, (int)cols, threshold, A, flags, (hipStream_t)stream));
+}
+
+int int8_linear_forward_flagged(const void* A, int dtype, int64_t M, int64_t K, const uint32_t* flags,
+                                const int8_t* CB, const float* SCB, int64_t N, const void* bias, int32_t cap,
+                                void* out, int32_t* c32_debug, void* ws, size_t ws_bytes, void* stream) {
+  if (flags == nullptr && M > 0 && K > 0) return I8L_EINVAL;
+  return forward_impl(A, dtype, M, K, CB, SCB, N, bias, 0.0f, flags, cap, out, c32_debug, ws, ws_bytes, stream);
 }
 
 int int8_linear_forward_check(const void* ws, int64_t M, int64_t K, int32_t cap, void* stream, int32_t* count) {

@@ -9,10 +9,17 @@ namespace i8l {
 // Quantizer: X (rows x cols, dtype dt) -> codes, scale, outlier list (first
 // `cap` entries), count, sub (rows x cap fp16). scratch: quant_scratch_words()
 // 32-bit words.
+// preflags: column flag words ([slabs][words], the layout of the scratch)
+// handed over by the producer of X; the flags pass is then skipped.
 size_t quant_scratch_words(int64_t rows, int64_t cols);
 hipError_t launch_quantize(int dt, const void* X, int64_t rows, int cols, float tau, int8_t* codes, float* scale,
                            int32_t* idx, int32_t* count, uint16_t* sub, int cap, uint32_t* scratch,
-                           hipStream_t st);
+                           hipStream_t st, const uint32_t* preflags = nullptr);
+
+// Producer of a quantizer input: A = D(SiLU(H)) and A's column flag words
+// (quant_scratch_words(rows, cols) words) for tau.
+hipError_t launch_silu_flags(int dt, const void* H, int64_t rows, int cols, float tau, void* A, uint32_t* flags,
+                             hipStream_t st);
 
 // Forward GEMM with fused epilogue: out = D(CA.CB^T * SCA SCB / 127^2
 // + subA . Wdq[:, idx]^T + bias); optional int32 export of CA.CB^T.

@@ -102,6 +102,51 @@ __device__ __forceinline__ float mag_to_half_value(uint32_t m) {
   else return (float)(_Float16)bf16_to_f32((uint16_t)m);
 }
 
+// SiLU of the 8 elements of a raw chunk, rounded to the storage format, as raw
+// words (EasyDeL discussion #66: the activation between the MLP's linears).
+template <int DT>
+__device__ __forceinline__ void silu_chunk(v4u& a, v4u& b) {
+  auto f = [](float x) { return x / (1.0f + expf(-x)); };
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      a[d] = __float_as_uint(f(__uint_as_float(a[d])));
+      b[d] = __float_as_uint(f(__uint_as_float(b[d])));
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint16_t lo = (uint16_t)(a[d] & 0xffffu), hi = (uint16_t)(a[d] >> 16);
+      typedef typename Elem<DT>::T T;
+      const T rl = Elem<DT>::from_f32(f(Elem<DT>::to_f32(__builtin_bit_cast(T, lo))));
+      const T rh = Elem<DT>::from_f32(f(Elem<DT>::to_f32(__builtin_bit_cast(T, hi))));
+      a[d] = (uint32_t)__builtin_bit_cast(uint16_t, rl) | ((uint32_t)__builtin_bit_cast(uint16_t, rh) << 16);
+    }
+  }
+}
+
+// Store a raw 8-element chunk to row[c0 .. c0 + 7], clipped to cols.
+template <int DT>
+__device__ __forceinline__ void store_raw8(typename Elem<DT>::T* __restrict__ row, int c0, int cols, bool vec,
+                                           const v4u& a, const v4u& b) {
+  typedef typename Elem<DT>::T T;
+  if (vec && c0 + 8 <= cols) {
+    *reinterpret_cast<v4u*>(row + c0) = a;
+    if constexpr (DT == DT_F32) *reinterpret_cast<v4u*>(row + c0 + 4) = b;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (c0 + e < cols) {
+      if constexpr (DT == DT_F32) {
+        row[c0 + e] = __uint_as_float(e < 4 ? a[e] : b[e - 4]);
+      } else {
+        row[c0 + e] = __builtin_bit_cast(T, (uint16_t)(a[e >> 1] >> (16 * (e & 1))));
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // column flags: grid (ceil(cols / 64), slabs), 256 threads. Lane l reads the
 // 8-column chunk l & 7 of rows r0 + 8 * wave + (l >> 3) + 32 i; the running
@@ -109,10 +154,13 @@ __device__ __forceinline__ float mag_to_half_value(uint32_t m) {
 // and bf16). Lanes and waves sharing a chunk are then combined, the maxima
 // cast to fp16 once and compared with tau, and the workgroup writes words
 // 2 bx and 2 bx + 1 of bits[slab].
-template <int DT>
+// With ACT the kernel is also the producer of its input: it reads H, stores
+// X = SiLU(H) (rounded to the storage format) and flags the columns of X.
+template <int DT, bool ACT = false>
 __global__ __launch_bounds__(256) void k_colflags(const typename Elem<DT>::T* __restrict__ X, int64_t rows,
                                                   int cols, float tau, int64_t rows_per_slab, int vec, int nwords,
-                                                  uint32_t* __restrict__ bits) {
+                                                  uint32_t* __restrict__ bits,
+                                                  typename Elem<DT>::T* __restrict__ act_out = nullptr) {
   typedef typename Elem<DT>::T T;
   constexpr int NW = (DT == DT_F32) ? 8 : 4;   // words of magnitudes per 8-column chunk
   __shared__ uint32_t sm[4][8][NW];
@@ -141,6 +189,14 @@ __global__ __launch_bounds__(256) void k_colflags(const typename Elem<DT>::T* __
   };
   if (c0 < cols) {
     const bool fast = vec && c0 + 8 <= cols;
+    // with ACT the chunk of row r is activated and stored before it is flagged
+    auto consume = [&](int64_t row, v4u& a, v4u& b) {
+      if constexpr (ACT) {
+        silu_chunk<DT>(a, b);
+        store_raw8<DT>(act_out + row * (int64_t)cols, c0, cols, fast, a, b);
+      }
+      add(a, b);
+    };
     int64_t r = r0 + 8 * wave + ro;
     // groups of 8 rows (stride 32); the next group's loads are issued before
     // the current group is reduced
@@ -148,23 +204,25 @@ __global__ __launch_bounds__(256) void k_colflags(const typename Elem<DT>::T* __
       v4u a[8], b[8], na[8], nb[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) load_raw8<DT>(X + (r + 32 * u) * (int64_t)cols, c0, cols, fast, a[u], b[u]);
+      int64_t rg = r;
       for (r += 8 * 32; r + 7 * 32 < r1; r += 8 * 32) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) load_raw8<DT>(X + (r + 32 * u) * (int64_t)cols, c0, cols, fast, na[u], nb[u]);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          add(a[u], b[u]);
+          consume(rg + 32 * u, a[u], b[u]);
           a[u] = na[u];
           b[u] = nb[u];
         }
+        rg = r;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) add(a[u], b[u]);
+      for (int u = 0; u < 8; ++u) consume(rg + 32 * u, a[u], b[u]);
     }
     for (; r < r1; r += 32) {
       v4u a, b;
       load_raw8<DT>(X + r * (int64_t)cols, c0, cols, fast, a, b);
-      add(a, b);
+      consume(r, a, b);
     }
   }
   // lanes with the same chunk: xor over the row-offset bits of the lane id
@@ -520,19 +578,22 @@ size_t quant_scratch_words(int64_t rows, int64_t cols) {
 template <int DT>
 static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, float tau, int8_t* codes,
                                     float* scale, int32_t* idx, int32_t* count, uint16_t* sub, int cap,
-                                    uint32_t* scratch, hipStream_t st) {
+                                    uint32_t* scratch, const uint32_t* preflags, hipStream_t st) {
   typedef typename Elem<DT>::T T;
   const T* X = static_cast<const T*>(Xv);
-  const bool tau_on = (tau > 0.0f) && (tau < __builtin_huge_valf()) && rows > 0 && cols > 0;
+  // column flags handed over by the producer of X replace the flags pass
+  const bool tau_on = (preflags != nullptr || ((tau > 0.0f) && (tau < __builtin_huge_valf()))) && rows > 0 &&
+                      cols > 0;
   const int nwords = (cols + 31) / 32;
   const int vec = (cols % 8 == 0) && aligned(X, 16) && aligned(codes, 8);
   const int slabs = colflag_slabs(rows, cols);
-  if (tau_on) {
+  if (tau_on && preflags == nullptr) {
     const int gx = (cols + CF_COLS - 1) / CF_COLS;
     const int64_t rps = (rows + slabs - 1) / slabs;
     hipLaunchKernelGGL(k_colflags<DT>, dim3(gx, (unsigned)slabs), dim3(256), 0, st, X, rows, cols, tau, rps, vec,
-                       nwords, scratch);
+                       nwords, scratch, nullptr);
   }
+  const uint32_t* bits = preflags != nullptr ? preflags : scratch;
   // the row kernel also writes the outlier list and count (count 0 when the split is off)
   const int64_t rblocks = rows > 0 ? (rows + 3) / 4 : 1;
   dim3 grid((unsigned)(rblocks < RQ_MAX_BLOCKS ? rblocks : RQ_MAX_BLOCKS));
@@ -546,7 +607,7 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
       hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (e != hipSuccess) return e;                                                                            \
     }                                                                                                           \
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, X, rows, cols, (int)tau_on, scratch, slabs, codes, scale,  \
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, X, rows, cols, (int)tau_on, bits, slabs, codes, scale,     \
                        idx, count, sub, cap);                                                                   \
   } while (0)
   // rows of up to 4096 16-bit values stay in registers; fp32, wider, unaligned
@@ -568,11 +629,42 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
 
 hipError_t launch_quantize(int dt, const void* X, int64_t rows, int cols, float tau, int8_t* codes, float* scale,
                            int32_t* idx, int32_t* count, uint16_t* sub, int cap, uint32_t* scratch,
-                           hipStream_t st) {
+                           hipStream_t st, const uint32_t* preflags) {
   switch (dt) {
-    case DT_F32: return launch_quantize_t<DT_F32>(X, rows, cols, tau, codes, scale, idx, count, sub, cap, scratch, st);
-    case DT_F16: return launch_quantize_t<DT_F16>(X, rows, cols, tau, codes, scale, idx, count, sub, cap, scratch, st);
-    default: return launch_quantize_t<DT_BF16>(X, rows, cols, tau, codes, scale, idx, count, sub, cap, scratch, st);
+    case DT_F32:
+      return launch_quantize_t<DT_F32>(X, rows, cols, tau, codes, scale, idx, count, sub, cap, scratch, preflags, st);
+    case DT_F16:
+      return launch_quantize_t<DT_F16>(X, rows, cols, tau, codes, scale, idx, count, sub, cap, scratch, preflags, st);
+    default:
+      return launch_quantize_t<DT_BF16>(X, rows, cols, tau, codes, scale, idx, count, sub, cap, scratch, preflags, st);
+  }
+}
+
+template <int DT>
+static hipError_t launch_silu_flags_t(const void* Hv, int64_t rows, int cols, float tau, void* Av, uint32_t* flags,
+                                      hipStream_t st) {
+  typedef typename Elem<DT>::T T;
+  const T* H = static_cast<const T*>(Hv);
+  T* A = static_cast<T*>(Av);
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  // with the split off no column is flagged: compare against +inf
+  const bool tau_on = (tau > 0.0f) && (tau < __builtin_huge_valf());
+  const int nwords = (cols + 31) / 32;
+  const int vec = (cols % 8 == 0) && aligned(H, 16) && aligned(A, 16);
+  const int slabs = colflag_slabs(rows, cols);
+  const int gx = (cols + CF_COLS - 1) / CF_COLS;
+  const int64_t rps = (rows + slabs - 1) / slabs;
+  hipLaunchKernelGGL((k_colflags<DT, true>), dim3(gx, (unsigned)slabs), dim3(256), 0, st, H, rows, cols,
+                     tau_on ? tau : __builtin_huge_valf(), rps, vec, nwords, flags, A);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_flags(int dt, const void* H, int64_t rows, int cols, float tau, void* A, uint32_t* flags,
+                             hipStream_t st) {
+  switch (dt) {
+    case DT_F32: return launch_silu_flags_t<DT_F32>(H, rows, cols, tau, A, flags, st);
+    case DT_F16: return launch_silu_flags_t<DT_F16>(H, rows, cols, tau, A, flags, st);
+    default: return launch_silu_flags_t<DT_BF16>(H, rows, cols, tau, A, flags, st);
   }
 }
 

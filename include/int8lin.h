@@ -140,7 +140,8 @@ int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const in
  * words for an input of rows x cols (row slabs x ceil(cols / 32) words).
  *
  * int8_silu_outlier_flags: A = D(SiLU(H)) elementwise, SiLU(x) = x / (1 +
- * exp(-x)) evaluated in fp32 and rounded once to `dtype`; flags = the
+ * exp(-x)) evaluated in fp32 (within four fp32 units in the last place) and
+ * rounded once to `dtype`; flags = the
  * outlier-column flags of A for `threshold` (a column is flagged when any row
  * has |fp16(A)| > threshold; threshold <= 0, +inf or NaN flags nothing).
  * H, A: rows x cols of `dtype` (A may not overlap H); flags: the caller's

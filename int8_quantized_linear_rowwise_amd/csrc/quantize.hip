@@ -104,9 +104,15 @@ __device__ __forceinline__ float mag_to_half_value(uint32_t m) {
 
 // SiLU of the 8 elements of a raw chunk, rounded to the storage format, as raw
 // words (EasyDeL discussion #66: the activation between the MLP's linears).
+// fp32 results use the accurate exp and IEEE division; for 16-bit results the
+// hardware exp and reciprocal (a few fp32 ulps) are far inside one unit of
+// the output format.
 template <int DT>
 __device__ __forceinline__ void silu_chunk(v4u& a, v4u& b) {
-  auto f = [](float x) { return x / (1.0f + expf(-x)); };
+  auto f = [](float x) {
+    if constexpr (DT == DT_F32) return x / (1.0f + expf(-x));
+    else return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+  };
   if constexpr (DT == DT_F32) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {

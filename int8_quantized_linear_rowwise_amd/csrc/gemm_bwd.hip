@@ -18,10 +18,6 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
-#ifndef I8L_BWD_WAVES
-#define I8L_BWD_WAVES 8
-#endif
-
 namespace i8l {
 
 
@@ -232,267 +228,13 @@ __global__ __launch_bounds__(256) void k_gemm_bwd(const typename Elem<DT>::T* __
 }
 
 // Large-tile backward kernel for 16-bit gradients: 256 (m) x 256 (k) output
-// tile, 4 waves of 128 x 128, the contraction over n stepped 64 at a time
-// through two swizzled LDS stages of 64 KB (W^T tile: 256 k-rows x 64 n,
-// G tile: 256 m-rows x 64 n, both fp16). Per stage each wave runs 64 MFMAs;
-// the next stage's int8 weights and gradient come in through buffer loads at
-// the start of the stage and are dequantized / converted and written to the
-// other LDS stage in the following phases, interleaved with the MFMAs.
-// Requires N % 8 == 0 and K % 4 == 0.
-template <int DT, bool OV>
-__global__ __launch_bounds__(256, 1) void k_gemm_bwd_big(const typename Elem<DT>::T* __restrict__ G, int M, int N,
-                                                         const int8_t* __restrict__ CB,
-                                                         const float* __restrict__ SCB, int K,
-                                                         typename Elem<DT>::T* __restrict__ gA) {
-  static_assert(DT == DT_F16 || DT == DT_BF16, "16-bit gradients only");
-  constexpr int BM = 256, BK = 256, BNC = 64, TI = 4, TJ = 4;
-  constexpr int ROW = BNC * 2;                 // bytes per LDS row
-  constexpr int STAGE = (BK + BM) * ROW;       // 64 KB
-  constexpr int GOFF = BK * ROW;               // G tile after the W^T tile
-  extern __shared__ __attribute__((aligned(16))) char bsm[];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 31, lg = lane >> 5;
-  const int wk = wave & 1, wm = wave >> 1;
-
-  const int tiles_m = (M + BM - 1) / BM, tiles_k = (K + BK - 1) / BK;
-  int tm, tk;
-  tile_coords(blockIdx.x, tiles_m, tiles_k, tm, tk);
-  const int m0 = tm * BM, k0 = tk * BK;
-
-  const __amdgpu_buffer_rsrc_t rG = make_rsrc(G + (int64_t)m0 * N, min(BM, M - m0) * N * 2);
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(CB + k0, N * K - k0);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(SCB, N * 4);
-
-  // G slots: 16-byte chunk gc of rows grow + 32 i. Wave-uniform parts of the
-  // offsets go to the scalar offset operand of the buffer loads.
-  const int grow = tid >> 3, gc = tid & 7;
-  const int gvoff = grow * N * 2 + 16 * gc;
-  const int gwoff = GOFF + grow * ROW + 16 * (gc ^ lds_swz(grow));
-  // W units: 8 consecutive n (wave-uniform group ng = wave + 4 u) x 4 consecutive k (per lane)
-  const int kq = tid & 63;
-  const int wvoff = 4 * kq;
-  int wwoff[2][4];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int r = 4 * kq + c;
-      wwoff[u][c] = r * ROW + 16 * ((wave + 4 * u) ^ lds_swz(r));
-    }
-
-  const int sw = lds_swz(lr);
-  int roff[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) roff[ks] = lr * ROW + 16 * ((2 * ks + lg) ^ sw);
-  const int pb = wk * 128 * ROW, qb = GOFF + wm * 128 * ROW;
-
-  v4u RG[8];
-  uint32_t RW[2][8];
-  float SG[2][8];
-
-  // Rows n >= N lie past the end of the weight buffer and read as zero.
-  // Columns k >= K of the last tile read the next row's bytes: they only reach
-  // output columns k >= K, which are never stored.
-  auto load_w = [&](int u, int nc) {
-    const int n8 = nc + 8 * (wave + 4 * u);        // wave-uniform; N % 8 == 0
-#pragma unroll
-    for (int e = 0; e < 8; ++e) RW[u][e] = __builtin_amdgcn_raw_buffer_load_b32(rW, wvoff, (n8 + e) * K, 0);
-    const int so = (n8 < N) ? 4 * n8 : OOB_OFFSET;
-    const v4f s0 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rS, so, 0, 0));
-    const v4f s1 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rS, so + 16, 0, 0));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      SG[u][e] = s0[e];
-      SG[u][4 + e] = s1[e];
-    }
-  };
-  // gradient chunks past N (contraction tail) must read as zero: out of range
-  auto load_g = [&](int h, int nc) {
-    const int gv = (nc + 8 * gc < N) ? gvoff : OOB_OFFSET;
-#pragma unroll
-    for (int i = 4 * h; i < 4 * h + 4; ++i)
-      RG[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rG, gv, 2 * nc + 64 * i * N, 0));
-  };
-  // Wdq[n, k] = fp16(CB[n, k] * fl32(SCB[n] * fl32(1/127))), written transposed
-  auto write_w = [&](int st, int u) {
-    float sg[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sg[e] = SG[u][e] * (1.0f / 127.0f);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v4u h;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float w0 = (float)(int)(int8_t)(RW[u][2 * e] >> (8 * c));
-        const float w1 = (float)(int)(int8_t)(RW[u][2 * e + 1] >> (8 * c));
-        h[e] = f32x2_to_f16x2(w0 * sg[2 * e], w1 * sg[2 * e + 1]);
-      }
-      *reinterpret_cast<v4u*>(bsm + st * STAGE + wwoff[u][c]) = h;
-    }
-  };
-  auto write_g = [&](int st, int h) {
-#pragma unroll
-    for (int i = 4 * h; i < 4 * h + 4; ++i) {
-      v4u v;
-      if constexpr (DT == DT_F16) {
-        v = RG[i];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(RG[i][e]);
-      }
-      *reinterpret_cast<v4u*>(bsm + st * STAGE + gwoff + i * 32 * ROW) = v;
-    }
-  };
-
-  v16f acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
-
-  v8h F[2][8];
-  auto fread = [&](int st, int ks, int b) {
-    const char* base = bsm + st * STAGE + roff[ks];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) F[b][i] = *reinterpret_cast<const v8h*>(base + pb + i * 32 * ROW);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) F[b][4 + j] = *reinterpret_cast<const v8h*>(base + qb + j * 32 * ROW);
-  };
-  auto mma = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F[b][i], F[b][4 + j], acc[i][j], 0, 0, 0);
-  };
-
-  // Software pipeline: LDS stage t&1 holds chunk t while registers hold the
-  // raw chunk t+1; each quarter of iteration t converts one quarter of the
-  // registers into the other LDS stage and reloads it with chunk t+2.
-  const int nn = (N + BNC - 1) / BNC;
-  load_w(0, 0);
-  load_w(1, 0);
-  load_g(0, 0);
-  load_g(1, 0);
-  write_w(0, 0);
-  write_w(0, 1);
-  write_g(0, 0);
-  write_g(0, 1);
-  load_w(0, BNC);
-  load_w(1, BNC);
-  load_g(0, BNC);
-  load_g(1, BNC);
-  __syncthreads();
-  fread(0, 0, 0);
-  for (int t = 0; t < nn; ++t) {
-    const int st = t & 1;
-    const int nc2 = (t + 2) * BNC;   // past the end: zeros
-    fread(st, 1, 1);
-    write_w(st ^ 1, 0);
-    load_w(0, nc2);
-    mma(0);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-      I8L_SGB(SG_VALU, 5);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_VALU, 5);
-      I8L_SGB(SG_DS_W, 1);
-      I8L_SGB(SG_VMEM_R, 2);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    fread(st, 2, 0);
-    write_w(st ^ 1, 1);
-    load_w(1, nc2);
-    mma(1);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-      I8L_SGB(SG_VALU, 5);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_VALU, 5);
-      I8L_SGB(SG_DS_W, 1);
-      I8L_SGB(SG_VMEM_R, 2);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    fread(st, 3, 1);
-    write_g(st ^ 1, 0);
-    load_g(0, nc2);
-    mma(0);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-      I8L_SGB(SG_VALU, 3);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_VALU, 3);
-      I8L_SGB(SG_DS_W, 1);
-      I8L_SGB(SG_VMEM_R, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    write_g(st ^ 1, 1);
-    load_g(1, nc2);
-    mma(1);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_VALU, 2);
-      I8L_SGB(SG_DS_W, 1);
-      I8L_SGB(SG_VMEM_R, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    fread(st ^ 1, 0, 0);
-  }
-
-  // lane (lr, lg), register r of tile (i, j):
-  //   k = k0 + wk*128 + i*32 + (r/4)*8 + lg*4 + r%4,  m = m0 + wm*128 + j*32 + lr
-  typedef typename Elem<DT>::T T;
-  const int kb = k0 + wk * 128 + lg * 4;
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int m = m0 + wm * 128 + j * 32 + lr;
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = kb + i * 32 + q * 8;
-        T* p = gA + (int64_t)m * K + k;
-        T v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = Elem<DT>::from_f32(acc[i][j][4 * q + e]);
-        if (OV && k + 3 < K) {
-          v2u w;
-          w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
-          w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
-          *reinterpret_cast<v2u*>(p) = w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (k + e < K) p[e] = v[e];
-        }
-      }
-    }
-  }
-}
-
-// Eight-wave variant of the large-tile backward kernel: the same 256 x 256
-// tile and LDS stages, but 8 waves (two per SIMD) of 128 (k) x 64 (m) each, so
-// that one wave's MFMAs run while the other waits on its loads.
+// tile, 8 waves (two per SIMD, so that one wave's MFMAs run while the other
+// waits) of 128 (k) x 64 (m), the contraction over n stepped 64 at a time
+// through two swizzled LDS stages of 64 KB (W^T tile: 256 k-rows x 64 n, G
+// tile: 256 m-rows x 64 n, both fp16). The next stage's int8 weights and
+// gradient come in through buffer loads two steps ahead and are dequantized /
+// cast and written to the other LDS stage in the first phases of a step,
+// between the MFMAs. Requires N % 8 == 0 and K % 4 == 0.
 template <int DT, bool OV>
 __global__ __launch_bounds__(512, 1) void k_gemm_bwd_w8(const typename Elem<DT>::T* __restrict__ G, int M, int N,
                                                         const int8_t* __restrict__ CB,
@@ -690,23 +432,6 @@ static hipError_t launch_bwd_w8(const void* G, int M, int N, const int8_t* CB, c
   return hipGetLastError();
 }
 
-template <int DT, bool OV>
-static hipError_t launch_bwd_big(const void* G, int M, int N, const int8_t* CB, const float* SCB, int K, void* gA,
-                                 hipStream_t st) {
-  typedef typename Elem<DT>::T T;
-  constexpr size_t lds = (size_t)2 * (256 + 256) * 128;
-  auto kern = k_gemm_bwd_big<DT, OV>;
-  static std::atomic<uint64_t> lds_set{0};
-  {
-    const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
-    if (e != hipSuccess) return e;
-  }
-  const int tiles = ((M + 255) / 256) * ((K + 255) / 256);
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, static_cast<const T*>(G), M, N, CB, SCB, K,
-                     static_cast<T*>(gA));
-  return hipGetLastError();
-}
-
 template <int BM, int BK, int BNC, int DT, bool GV, bool WV, bool OV>
 static hipError_t launch_bwd_cfg(const void* G, int M, int N, const int8_t* CB, const float* SCB, int K, void* gA,
                                  hipStream_t st) {
@@ -742,13 +467,8 @@ hipError_t launch_gemm_bwd(int dt, const void* G, int M, int N, const int8_t* CB
                     (int64_t)N * 2 * 256 < ((int64_t)1 << 31) - 4096;
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((K + 255) / 256);
   if (dt != DT_F32 && gv && wv && ov && fits && big_tiles >= 64) {
-#if I8L_BWD_WAVES == 4
-    if (dt == DT_F16) return launch_bwd_big<DT_F16, true>(G, M, N, CB, SCB, K, gA, st);
-    return launch_bwd_big<DT_BF16, true>(G, M, N, CB, SCB, K, gA, st);
-#else
     if (dt == DT_F16) return launch_bwd_w8<DT_F16, true>(G, M, N, CB, SCB, K, gA, st);
     return launch_bwd_w8<DT_BF16, true>(G, M, N, CB, SCB, K, gA, st);
-#endif
   }
 #define I8L_BWD(D)                                                                   \
   do {                                                                               \

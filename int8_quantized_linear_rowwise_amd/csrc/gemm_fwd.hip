@@ -19,10 +19,6 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
-#ifndef I8L_FWD_WAVES
-#define I8L_FWD_WAVES 8
-#endif
-
 namespace i8l {
 
 
@@ -340,147 +336,7 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(const int8_t* __restrict__ CA,
                                count, bias, out, c32);
 }
 
-// Large-tile forward kernel: 256 x 256 output tile, 4 waves of 128 x 128,
-// K stepped 128 bytes at a time through two swizzled LDS stages (64 KB each).
-// Global tiles come in through buffer loads (rows past M / N and columns past
-// K read as zero), are held in registers for one step and written to the
-// other stage; operand fragments are double-buffered in registers so that
-// LDS reads of the next 32-wide k slice overlap the MFMAs of the current one.
-// Requires K % 16 == 0.
-template <int DT, bool OV>
-__global__ __launch_bounds__(256, 1) void k_gemm_fwd_big(const int8_t* __restrict__ CA,
-                                                         const float* __restrict__ SCA, int M,
-                                                         const int8_t* __restrict__ CB,
-                                                         const float* __restrict__ SCB, int N, int K,
-                                                         const uint16_t* __restrict__ subA, int cap,
-                                                         const int32_t* __restrict__ idx,
-                                                         const int32_t* __restrict__ count,
-                                                         const typename Elem<DT>::T* __restrict__ bias,
-                                                         typename Elem<DT>::T* __restrict__ out,
-                                                         int32_t* __restrict__ c32) {
-  constexpr int BM = 256, BN = 256, BK = 128, TI = 4, TJ = 4;
-  constexpr int STAGE = (BM + BN) * BK;        // bytes per LDS stage
-  constexpr int AOFF = BN * BK;                // A tile after the B tile
-  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 31, lg = lane >> 5;
-  const int wn = wave & 1, wm = wave >> 1;
-
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(CA + (int64_t)m0 * K, min(BM, M - m0) * K);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(CB + (int64_t)n0 * K, min(BN, N - n0) * K);
-
-  // global -> register slots: chunk c (16 bytes) of rows lrow + 32 i
-  const int lrow = tid >> 3, lc = tid & 7;
-  const int voff = lrow * K + 16 * lc;
-  const int woff = lrow * BK + 16 * (lc ^ lds_swz(lrow));
-  // fragment read offsets for the four 32-byte k slices of a stage
-  const int sw = lds_swz(lr);
-  int roff[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) roff[ks] = lr * BK + 16 * ((2 * ks + lg) ^ sw);
-  const int pb = wn * 128 * BK, qb = AOFF + wm * 128 * BK;
-
-  v4u R[16];
-  auto gload = [&](int kt) {
-    // chunks past K (contraction tail) must read as zero: push them out of range
-    const int keep = -(int)(kt + 16 * lc < K);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int oi = ((voff + kt + 32 * i * K) & keep) | (OOB_OFFSET & ~keep);
-      R[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rB, oi, 0, 0));
-      R[8 + i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rA, oi, 0, 0));
-    }
-  };
-  auto swrite = [&](int st) {
-    int8_t* b = smem + st * STAGE + woff;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<v4u*>(b + i * 32 * BK) = R[i];
-      *reinterpret_cast<v4u*>(b + AOFF + i * 32 * BK) = R[8 + i];
-    }
-  };
-
-  v16i acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
-
-  v4i F[2][8];
-  auto fread = [&](int st, int ks, int b) {
-    const int8_t* base = smem + st * STAGE + roff[ks];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) F[b][i] = *reinterpret_cast<const v4i*>(base + pb + i * 32 * BK);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) F[b][4 + j] = *reinterpret_cast<const v4i*>(base + qb + j * 32 * BK);
-  };
-  auto mma = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[b][i], F[b][4 + j], acc[i][j], 0, 0, 0);
-  };
-
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  fread(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    gload((kt + 1) * BK);          // past the end: all offsets out of range, zeros
-    fread(st, 1, 1);
-    mma(0);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-      I8L_SGB(SG_VMEM_R, 2);
-    }
-    I8L_SGB(SG_MFMA, 8);
-    __builtin_amdgcn_sched_barrier(0);
-    fread(st, 2, 0);
-    mma(1);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-    }
-    I8L_SGB(SG_MFMA, 8);
-    __builtin_amdgcn_sched_barrier(0);
-    fread(st, 3, 1);
-    mma(0);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-    }
-    I8L_SGB(SG_MFMA, 8);
-    __builtin_amdgcn_sched_barrier(0);
-    swrite(st ^ 1);
-    mma(1);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_W, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    fread(st ^ 1, 0, 0);
-  }
-
-  fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 128, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, idx,
-                               count, bias, out, c32);
-}
-
-// Eight-wave large-tile forward kernel: 256 x 256 output tile, 8 waves (two
+// Large-tile forward kernel: 256 x 256 output tile, 8 waves (two
 // per SIMD) of 128 (n) x 64 (m), K stepped 128 bytes at a time through two
 // swizzled LDS stages of 64 KB. Registers hold the next step's tiles; each
 // of the first two quarters of a step writes half of them to the other stage
@@ -731,24 +587,6 @@ static hipError_t launch_fwd_cfg(const int8_t* CA, const float* SCA, int M, cons
   return hipGetLastError();
 }
 
-template <int DT, bool OV>
-static hipError_t launch_fwd_big(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                                 int N, int K, const uint16_t* subA, int cap, const int32_t* idx,
-                                 const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
-  typedef typename Elem<DT>::T T;
-  constexpr size_t lds = (size_t)2 * (256 + 256) * 128;
-  auto kern = k_gemm_fwd_big<DT, OV>;
-  static std::atomic<uint64_t> lds_set{0};
-  {
-    const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
-    if (e != hipSuccess) return e;
-  }
-  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count,
-                     static_cast<const T*>(bias), static_cast<T*>(out), c32);
-  return hipGetLastError();
-}
-
 template <int DT, bool KV, bool OV>
 static hipError_t launch_fwd_dt(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
                                 int N, int K, const uint16_t* subA, int cap, const int32_t* idx, const int32_t* count,
@@ -756,11 +594,7 @@ static hipError_t launch_fwd_dt(const int8_t* CA, const float* SCA, int M, const
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   if constexpr (KV) {
     if (big_tiles >= 64) {
-#if I8L_FWD_WAVES == 4
-      return launch_fwd_big<DT, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st);
-#else
       return launch_fwd_w8<DT, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st);
-#endif
     }
   }
   return launch_fwd_cfg<128, 128, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32,

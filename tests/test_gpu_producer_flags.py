@@ -120,3 +120,45 @@ def test_mlp_chain_through_producer_flags(I8, dt):
     assert f2["q"]["outliers"].size >= 1
     assert_bits_equal(host(c32), f2["c32"].astype(np.int32), "layer-2 C32")
     assert_float_gate(host(y), dt, f2["y"], "layer-2 out")
+
+
+def test_full_size_down_projection_input(I8):
+    """The 7B-class block's widest input (4096 tokens x 11008, bf16): the SiLU
+    kernel's flags bit-exact against the oracle's outlier columns of its A,
+    and the flagged forward bit-identical to the ordinary one."""
+    wl = workloads.WORKLOADS["llama7b_block"]
+    li = [i for i, L in enumerate(wl.layers) if L.name == "down"][0]
+    L = wl.layers[li]
+    print(f"\n[llama7b_block/{L.name} input] {L.M} x {L.K} bf16", flush=True)
+    H = workloads.make_activation(wl, li)
+    A, flags = I8.silu_outlier_flags(dev(H, "bf16"), wl.threshold)
+    torch.cuda.synchronize()
+    Ah = host(A)
+    want = oracle.outlier_columns(to_half(Ah, "bf16"), wl.threshold)
+    assert want.size >= 1
+    assert_bits_equal(_mask(I8, flags, L.M, L.K), want, "outlier columns of A")
+    rows = np.array([0, 1, 2047, L.M - 1])
+    y = oracle.silu_activation(H[rows], "bf16")["y"]
+    a = to_f64(Ah[rows], "bf16")
+    assert np.all(np.abs(a - y) <= ulp(np.abs(y), "bf16") + 1e-300)
+    W = workloads.make_weight(wl, li)
+    CB, SCB = I8.quantize_weight(dev(W))
+    del W
+    o1 = I8.int8_linear_forward(A, CB, SCB, None, wl.threshold)
+    o2 = I8.int8_linear_forward_flagged(A, flags, CB, SCB, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_flagged_forward_reports_overflow(I8):
+    """More flagged columns than the outlier buffer holds: the same overflow
+    report as the ordinary forward."""
+    M, K, N = 40, 64, 32
+    H = _H("f16", M, K, 5, hot=6)
+    A, flags = I8.silu_outlier_flags(dev(H, "f16"), 6.0)
+    CB, SCB = I8.quantize_weight(torch.randn(N, K, device="cuda:0") * 0.02)
+    ws = I8.forward_workspace(M, K, 2, "cuda:0")
+    I8.int8_linear_forward_flagged(A, flags, CB, SCB, None, cap=2, workspace=ws)
+    with pytest.raises(I8.Int8LinError) as e:
+        I8.forward_check(ws, M, K, 2)
+    assert e.value.code == -6

@@ -145,23 +145,25 @@ int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const in
  * outlier-column flags of A for `threshold` (a column is flagged when any row
  * has |fp16(A)| > threshold; threshold <= 0, +inf or NaN flags nothing).
  * H, A: rows x cols of `dtype` (A may not overlap H); flags: the caller's
- * buffer of int8_outlier_flags_words(rows, cols) words, fully overwritten.
+ * buffer of flag_words >= int8_outlier_flags_words(rows, cols) words, fully
+ * overwritten (I8L_EWORKSPACE when smaller).
  *
  * int8_linear_forward_flagged: int8_linear_forward with the outlier columns
  * given by `flags` (from int8_silu_outlier_flags on the same rows x K shape;
  * the threshold is the one the flags were made with) instead of found by a
  * pass over A. Same workspace, outputs and errors as int8_linear_forward;
- * flags NULL (with M, K > 0) is I8L_EINVAL.
+ * flags NULL (with M, K > 0) is I8L_EINVAL, flag_words below
+ * int8_outlier_flags_words(M, K) is I8L_EWORKSPACE.
  * ------------------------------------------------------------------------ */
 size_t int8_outlier_flags_words(int64_t rows, int64_t cols);
 
 int int8_silu_outlier_flags(const void* H, int dtype, int64_t rows, int64_t cols, float threshold, void* A,
-                            uint32_t* flags, void* stream);
+                            uint32_t* flags, size_t flag_words, void* stream);
 
 int int8_linear_forward_flagged(const void* A, int dtype, int64_t M, int64_t K, const uint32_t* flags,
-                                const int8_t* CB, const float* SCB, int64_t N, const void* bias, int32_t cap,
-                                void* out, int32_t* c32_debug, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                size_t flag_words, const int8_t* CB, const float* SCB, int64_t N, const void* bias,
+                                int32_t cap, void* out, int32_t* c32_debug, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Synchronises `stream`, reads the outlier count of the last forward that used
  * `workspace` and returns I8L_EOVERFLOW if it exceeded `cap` (the output of

@@ -184,7 +184,7 @@ def silu_outlier_flags(H: torch.Tensor, threshold: float = 6.0, A: Optional[torc
     elif flags.dtype != torch.int32 or flags.numel() < n:
         raise ValueError(f"flags must be int32 with at least {n} elements")
     check(lib.int8_silu_outlier_flags(_dev(H, "H"), _code(H), R, C, float(threshold), _dev(A, "A"),
-                                      _dev(flags, "flags"), _stream(H.device)),
+                                      _dev(flags, "flags"), flags.numel(), _stream(H.device)),
           "int8_silu_outlier_flags")
     return A, flags
 
@@ -211,7 +211,8 @@ def int8_linear_forward_flagged(A: torch.Tensor, flags: torch.Tensor, CB: torch.
         out = _empty((M, N), A.dtype, A.device)
     if workspace is None:
         workspace = forward_workspace(M, K, cap, A.device)
-    check(lib.int8_linear_forward_flagged(_dev(A, "A"), _code(A), M, K, _dev(flags, "flags"), _dev(CB, "CB"),
+    check(lib.int8_linear_forward_flagged(_dev(A, "A"), _code(A), M, K, _dev(flags, "flags"), flags.numel(),
+                                          _dev(CB, "CB"),
                                           _dev(SCB, "SCB"), N, _dev(bias, "bias"), cap, _dev(out, "out"),
                                           _dev(c32, "c32"), workspace.data_ptr(), workspace.numel(),
                                           _stream(A.device)),

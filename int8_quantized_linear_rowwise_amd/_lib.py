@@ -41,9 +41,9 @@ SIGNATURES = {
                                                _vp]),
     "int8_linear_backward_weight": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _vp, _vp]),
     "int8_outlier_flags_words": (_sz, [_i64, _i64]),
-    "int8_silu_outlier_flags": (_int, [_vp, _int, _i64, _i64, _f32, _vp, _vp, _vp]),
-    "int8_linear_forward_flagged": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp,
-                                           _sz, _vp]),
+    "int8_silu_outlier_flags": (_int, [_vp, _int, _i64, _i64, _f32, _vp, _vp, _sz, _vp]),
+    "int8_linear_forward_flagged": (_int, [_vp, _int, _i64, _i64, _vp, _sz, _vp, _vp, _i64, _vp, _i32, _vp, _vp,
+                                           _vp, _sz, _vp]),
 }
 
 

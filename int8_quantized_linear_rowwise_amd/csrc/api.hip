@@ -15,7 +15,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool valid_dtype(int dt) { return dt == I8L_F32 || dt == I8L_F16 || dt == I8L_BF16; }
 
-// quantizer scratch: per-slab column bits, column bitmask, per-word prefix
+// quantizer scratch: the column flag words of each row slab ([slabs][ceil(cols / 32)])
 size_t quant_scratch_bytes(int64_t rows, int64_t cols) { return align_up(i8l::quant_scratch_words(rows, cols) * 4); }
 
 bool fwd_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* L) {
@@ -134,19 +134,24 @@ size_t int8_outlier_flags_words(int64_t rows, int64_t cols) {
 }
 
 int int8_silu_outlier_flags(const void* H, int dtype, int64_t rows, int64_t cols, float threshold, void* A,
-                            uint32_t* flags, void* stream) {
+                            uint32_t* flags, size_t flag_words, void* stream) {
   if (!valid_dtype(dtype)) return I8L_EDTYPE;
   if (rows < 0 || cols < 0) return I8L_EINVAL;
   if (rows > INT32_MAX || cols > I8L_MAX_COLS || rows * cols > ((int64_t)1 << 40)) return I8L_ESHAPE;
   if (rows == 0 || cols == 0) return I8L_OK;
   if (H == nullptr || A == nullptr || flags == nullptr) return I8L_EINVAL;
+  if (flag_words < i8l::quant_scratch_words(rows, cols)) return I8L_EWORKSPACE;
   return hip_status(i8l::launch_silu_flags(dtype, H, rows, (int)cols, threshold, A, flags, (hipStream_t)stream));
 }
 
 int int8_linear_forward_flagged(const void* A, int dtype, int64_t M, int64_t K, const uint32_t* flags,
-                                const int8_t* CB, const float* SCB, int64_t N, const void* bias, int32_t cap,
-                                void* out, int32_t* c32_debug, void* ws, size_t ws_bytes, void* stream) {
-  if (flags == nullptr && M > 0 && K > 0) return I8L_EINVAL;
+                                size_t flag_words, const int8_t* CB, const float* SCB, int64_t N, const void* bias,
+                                int32_t cap, void* out, int32_t* c32_debug, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (M > 0 && K > 0) {
+    if (flags == nullptr) return I8L_EINVAL;
+    if (M <= INT32_MAX && K <= I8L_MAX_K && flag_words < i8l::quant_scratch_words(M, K)) return I8L_EWORKSPACE;
+  }
   return forward_impl(A, dtype, M, K, CB, SCB, N, bias, 0.0f, flags, cap, out, c32_debug, ws, ws_bytes, stream);
 }
 

@@ -196,28 +196,31 @@ def test_backward_weight_host_errors(L):
 
 def test_producer_flags_host_errors(L):
     f = L.lib.int8_silu_outlier_flags
-    assert f(FAKE, 9, 4, 8, 6.0, FAKE, FAKE, None) == L.I8L_EDTYPE
-    assert f(FAKE, 1, -1, 8, 6.0, FAKE, FAKE, None) == L.I8L_EINVAL
-    assert f(0, 1, 4, 8, 6.0, FAKE, FAKE, None) == L.I8L_EINVAL
-    assert f(FAKE, 1, 4, 8, 6.0, 0, FAKE, None) == L.I8L_EINVAL
-    assert f(FAKE, 1, 4, 8, 6.0, FAKE, 0, None) == L.I8L_EINVAL
-    assert f(FAKE, 1, 4, L.I8L_MAX_COLS + 1, 6.0, FAKE, FAKE, None) == L.I8L_ESHAPE
-    assert f(0, 1, 0, 8, 6.0, 0, 0, None) == L.I8L_OK            # nothing to do
     words = L.lib.int8_outlier_flags_words
+    nw = words(4, 8)
+    assert f(FAKE, 9, 4, 8, 6.0, FAKE, FAKE, nw, None) == L.I8L_EDTYPE
+    assert f(FAKE, 1, -1, 8, 6.0, FAKE, FAKE, nw, None) == L.I8L_EINVAL
+    assert f(0, 1, 4, 8, 6.0, FAKE, FAKE, nw, None) == L.I8L_EINVAL
+    assert f(FAKE, 1, 4, 8, 6.0, 0, FAKE, nw, None) == L.I8L_EINVAL
+    assert f(FAKE, 1, 4, 8, 6.0, FAKE, 0, nw, None) == L.I8L_EINVAL
+    assert f(FAKE, 1, 4, 8, 6.0, FAKE, FAKE, nw - 1, None) == L.I8L_EWORKSPACE
+    assert f(FAKE, 1, 4, L.I8L_MAX_COLS + 1, 6.0, FAKE, FAKE, 1 << 30, None) == L.I8L_ESHAPE
+    assert f(0, 1, 0, 8, 6.0, 0, 0, 0, None) == L.I8L_OK            # nothing to do
     assert words(4096, 4096) >= 4096 // 32 and words(4096, 4096) % (4096 // 32) == 0
     assert words(-1, 8) == 0
     g = L.lib.int8_linear_forward_flagged
     M, K, N = 8, 64, 32
     wsb = L.lib.int8_linear_forward_workspace_bytes(M, K, K)
-    base = dict(A=FAKE, dt=2, M=M, K=K, fl=FAKE, CB=FAKE, SCB=FAKE, N=N, b=None, cap=K, out=FAKE, c32=None, ws=FAKE,
-                wsb=wsb, st=None)
+    base = dict(A=FAKE, dt=2, M=M, K=K, fl=FAKE, fw=words(M, K), CB=FAKE, SCB=FAKE, N=N, b=None, cap=K, out=FAKE,
+                c32=None, ws=FAKE, wsb=wsb, st=None)
 
     def call(**kw):
         a = dict(base, **kw)
-        return g(a["A"], a["dt"], a["M"], a["K"], a["fl"], a["CB"], a["SCB"], a["N"], a["b"], a["cap"], a["out"],
-                 a["c32"], a["ws"], a["wsb"], a["st"])
+        return g(a["A"], a["dt"], a["M"], a["K"], a["fl"], a["fw"], a["CB"], a["SCB"], a["N"], a["b"], a["cap"],
+                 a["out"], a["c32"], a["ws"], a["wsb"], a["st"])
 
     assert call(fl=0) == L.I8L_EINVAL
+    assert call(fw=words(M, K) - 1) == L.I8L_EWORKSPACE
     assert call(dt=4) == L.I8L_EDTYPE
     assert call(wsb=wsb - 1) == L.I8L_EWORKSPACE
     assert call(K=L.I8L_MAX_K + 1, wsb=1 << 40) == L.I8L_ESHAPE

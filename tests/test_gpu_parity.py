@@ -51,8 +51,11 @@ def _check_quant(I8, X, dt, tau, cap=None):
     return q
 
 
-QSHAPES = [(1, 1), (3, 7), (17, 70), (64, 4096), (129, 4104), (5, 8200), (33, 11008), (2, 40000),
-           (600, 4), (600, 16), (1000, 64)]
+# rows of up to 4096 16-bit values stay in a wave's registers (several rows per
+# wave past 4096 rows); wider, ragged or fp32 rows stream through the cache
+# twice
+QSHAPES = [(1, 1), (3, 7), (17, 70), (64, 4096), (4100, 2048), (129, 4104), (5, 8200), (4100, 4104),
+           (33, 11008), (3, 20000), (2, 40000), (600, 4), (600, 16), (1000, 64)]
 
 
 @pytest.mark.parametrize("dt", DTS)

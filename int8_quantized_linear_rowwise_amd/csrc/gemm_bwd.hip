@@ -227,21 +227,26 @@ __global__ __launch_bounds__(256) void k_gemm_bwd(const typename Elem<DT>::T* __
   }
 }
 
-// Large-tile backward kernel for 16-bit gradients: 256 (m) x 256 (k) output
-// tile, 8 waves (two per SIMD, so that one wave's MFMAs run while the other
-// waits) of 128 (k) x 64 (m), the contraction over n stepped 64 at a time
-// through two swizzled LDS stages of 64 KB (W^T tile: 256 k-rows x 64 n, G
-// tile: 256 m-rows x 64 n, both fp16). The next stage's int8 weights and
-// gradient come in through buffer loads two steps ahead and are dequantized /
-// cast and written to the other LDS stage in the first phases of a step,
-// between the MFMAs. Requires N % 8 == 0 and K % 4 == 0.
-template <int DT, bool OV>
+// Large-tile backward kernel for 16-bit gradients: 256 (m) x BK (k) output
+// tile (BK = 256, or 128 when 256-wide tiles would leave compute units idle),
+// 8 waves (two per SIMD, so that one wave's MFMAs run while the other waits)
+// of BK / 2 (k) x 64 (m), the contraction over n stepped 64 at a time through
+// two swizzled LDS stages (W^T tile: BK k-rows x 64 n, G tile: 256 m-rows x
+// 64 n, both fp16). The next stage's int8 weights and gradient come in
+// through buffer loads two steps ahead and are dequantized / cast and written
+// to the other LDS stage in the first phases of a step, between the MFMAs.
+// Requires N % 8 == 0 and K % 4 == 0.
+template <int DT, bool OV, int BK = 256>
 __global__ __launch_bounds__(512, 1) void k_gemm_bwd_w8(const typename Elem<DT>::T* __restrict__ G, int M, int N,
                                                         const int8_t* __restrict__ CB,
                                                         const float* __restrict__ SCB, int K,
                                                         typename Elem<DT>::T* __restrict__ gA) {
   static_assert(DT == DT_F16 || DT == DT_BF16, "16-bit gradients only");
-  constexpr int BM = 256, BK = 256, BNC = 64, TI = 4, TJ = 2;
+  static_assert(BK == 256 || BK == 128, "256- or 128-wide tiles");
+  constexpr int BM = 256, BNC = 64, TI = BK / 64, TJ = 2;
+  // weight rows per lane: 8 (all 64 lanes on 4 k-bytes of each of the wave's
+  // 8 rows), or 4 with 128-wide tiles (half-waves on rows 0-3 and 4-7)
+  constexpr int WR = BK / 32;
   constexpr int ROW = BNC * 2;                 // bytes per LDS row
   constexpr int STAGE = (BK + BM) * ROW;       // 64 KB
   constexpr int GOFF = BK * ROW;               // G tile after the W^T tile
@@ -265,36 +270,39 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_w8(const typename Elem<DT>:
   const int grow = tid >> 3, gc = tid & 7;
   const int gvoff = grow * N * 2 + 16 * gc;
   const int gwoff = GOFF + grow * ROW + 16 * (gc ^ lds_swz(grow));
-  // W unit: rows n8 .. n8+7 with n8 = nc + 8*wave (wave-uniform), bytes 4kq .. 4kq+3
-  const int kq = tid & 63;
-  const int wvoff = 4 * kq;
+  // W unit: rows n8 + wh .. n8 + wh + WR - 1 with n8 = nc + 8*wave (wave-uniform),
+  // bytes 4kq .. 4kq+3; the 16-byte LDS chunk of the wave's 8 rows is
+  // written whole, or as two 8-byte halves
+  const int kq = BK == 256 ? (tid & 63) : (tid & 31);
+  const int wh = BK == 256 ? 0 : 4 * ((tid >> 5) & 1);
+  const int wvoff = 4 * kq + wh * K;
   int wwoff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int r = 4 * kq + c;
-    wwoff[c] = r * ROW + 16 * (wave ^ lds_swz(r));
+    wwoff[c] = r * ROW + 16 * (wave ^ lds_swz(r)) + 2 * wh;
   }
   const int sw = lds_swz(lr);
   int roff[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) roff[ks] = lr * ROW + 16 * ((2 * ks + lg) ^ sw);
-  const int pb = wk * 128 * ROW, qb = GOFF + wm * 64 * ROW;
+  const int pb = wk * (BK / 2) * ROW, qb = GOFF + wm * 64 * ROW;
 
   v4u RG[4];
-  uint32_t RW[8];
-  float SG[8];
+  uint32_t RW[WR];
+  float SG[WR];
 
   auto load_w = [&](int nc) {
     const int n8 = nc + 8 * wave;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) RW[e] = __builtin_amdgcn_raw_buffer_load_b32(rW, wvoff, (n8 + e) * K, 0);
-    const int so = (n8 < N) ? 4 * n8 : OOB_OFFSET;
-    const v4f s0 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rS, so, 0, 0));
-    const v4f s1 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rS, so + 16, 0, 0));
+    for (int e = 0; e < WR; ++e) RW[e] = __builtin_amdgcn_raw_buffer_load_b32(rW, wvoff, (n8 + e) * K, 0);
+    // N % 8 == 0: the eight rows from n8 are all in the matrix or all past it
+    const int so = (n8 < N) ? 4 * (n8 + wh) : OOB_OFFSET;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      SG[e] = s0[e];
-      SG[4 + e] = s1[e];
+    for (int h = 0; h < WR / 4; ++h) {
+      const v4f sv = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rS, so + 16 * h, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) SG[4 * h + e] = sv[e];
     }
   };
   auto load_g = [&](int nc) {
@@ -304,19 +312,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_w8(const typename Elem<DT>:
       RG[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rG, gv, 2 * nc + 128 * i * N, 0));
   };
   auto write_w = [&](int st, int c0) {
-    float sg[8];
+    float sg[WR];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sg[e] = SG[e] * (1.0f / 127.0f);
+    for (int e = 0; e < WR; ++e) sg[e] = SG[e] * (1.0f / 127.0f);
 #pragma unroll
     for (int c = c0; c < c0 + 2; ++c) {
-      v4u h;
+      uint32_t h[WR / 2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < WR / 2; ++e) {
         const float w0 = (float)(int)(int8_t)(RW[2 * e] >> (8 * c));
         const float w1 = (float)(int)(int8_t)(RW[2 * e + 1] >> (8 * c));
         h[e] = f32x2_to_f16x2(w0 * sg[2 * e], w1 * sg[2 * e + 1]);
       }
-      *reinterpret_cast<v4u*>(bsm + st * STAGE + wwoff[c]) = h;
+      if constexpr (WR == 8) *reinterpret_cast<v4u*>(bsm + st * STAGE + wwoff[c]) = v4u{h[0], h[1], h[2], h[3]};
+      else *reinterpret_cast<v2u*>(bsm + st * STAGE + wwoff[c]) = v2u{h[0], h[1]};
     }
   };
   auto write_g = [&](int st) {
@@ -390,7 +399,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_w8(const typename Elem<DT>:
   }
 
   // lane (lr, lg), register r of tile (i, j):
-  //   k = k0 + wk*128 + i*32 + (r/4)*8 + lg*4 + r%4,  m = m0 + wm*64 + j*32 + lr
+  //   k = k0 + wk*BK/2 + i*32 + (r/4)*8 + lg*4 + r%4,  m = m0 + wm*64 + j*32 + lr
   // The tile goes through LDS (row m, 16-byte chunk of 8 k) and leaves as
   // whole rows.
   typedef typename Elem<DT>::T T;
@@ -407,26 +416,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_w8(const typename Elem<DT>:
         for (int e = 0; e < 2; ++e)
           w[e] = (uint32_t)__builtin_bit_cast(uint16_t, Elem<DT>::from_f32(acc[i][j][4 * q + 2 * e])) |
                  ((uint32_t)__builtin_bit_cast(uint16_t, Elem<DT>::from_f32(acc[i][j][4 * q + 2 * e + 1])) << 16);
-        *reinterpret_cast<v2u*>(bsm + otile_off(row, wk * 16 + i * 4 + q) + 8 * lg) = w;
+        *reinterpret_cast<v2u*>(bsm + otile_off(row, wk * (BK / 16) + i * 4 + q) + 8 * lg) = w;
       }
     }
   }
   __syncthreads();
-  otile_store<T>(bsm, gA, K, m0, k0, M, K, wave, lane);
+  otile_store<T>(bsm, gA, K, m0, k0, M, BK == 256 ? K : min(K, k0 + BK), wave, lane);
 }
 
-template <int DT, bool OV>
+template <int DT, bool OV, int BK>
 static hipError_t launch_bwd_w8(const void* G, int M, int N, const int8_t* CB, const float* SCB, int K, void* gA,
                                 hipStream_t st) {
   typedef typename Elem<DT>::T T;
-  constexpr size_t lds = (size_t)2 * (256 + 256) * 128;
-  auto kern = k_gemm_bwd_w8<DT, OV>;
+  // both stages, or the output tile (256 rows of 512 bytes) if larger
+  constexpr size_t stages = (size_t)2 * (BK + 256) * 128, otile = (size_t)256 * 512;
+  constexpr size_t lds = stages > otile ? stages : otile;
+  auto kern = k_gemm_bwd_w8<DT, OV, BK>;
   static std::atomic<uint64_t> lds_set{0};
   {
     const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
   }
-  const int tiles = ((M + 255) / 256) * ((K + 255) / 256);
+  const int tiles = ((M + 255) / 256) * ((K + BK - 1) / BK);
   hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), lds, st, static_cast<const T*>(G), M, N, CB, SCB, K,
                      static_cast<T*>(gA));
   return hipGetLastError();
@@ -467,8 +478,14 @@ hipError_t launch_gemm_bwd(int dt, const void* G, int M, int N, const int8_t* CB
                     (int64_t)N * 2 * 256 < ((int64_t)1 << 31) - 4096;
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((K + 255) / 256);
   if (dt != DT_F32 && gv && wv && ov && fits && big_tiles >= 64) {
-    if (dt == DT_F16) return launch_bwd_w8<DT_F16, true>(G, M, N, CB, SCB, K, gA, st);
-    return launch_bwd_w8<DT_BF16, true>(G, M, N, CB, SCB, K, gA, st);
+    // 64 to 128 tiles of 256 x 256 would fill at most half of the 256 compute
+    // units: half-width tiles take about half the time each and fill them all
+    if (big_tiles <= 128) {
+      if (dt == DT_F16) return launch_bwd_w8<DT_F16, true, 128>(G, M, N, CB, SCB, K, gA, st);
+      return launch_bwd_w8<DT_BF16, true, 128>(G, M, N, CB, SCB, K, gA, st);
+    }
+    if (dt == DT_F16) return launch_bwd_w8<DT_F16, true, 256>(G, M, N, CB, SCB, K, gA, st);
+    return launch_bwd_w8<DT_BF16, true, 256>(G, M, N, CB, SCB, K, gA, st);
   }
 #define I8L_BWD(D)                                                                   \
   do {                                                                               \

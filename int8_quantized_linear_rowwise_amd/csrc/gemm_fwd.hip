@@ -16,6 +16,8 @@
 // same fp32 accumulators, then bias, cast and store. The product is computed
 // as C^T (weights on the MFMA's row side) so that each lane owns four
 // consecutive output features of one token and stores them as one vector.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -336,12 +338,13 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(const int8_t* __restrict__ CA,
                                count, bias, out, c32);
 }
 
-// Large-tile forward kernel: 256 x 256 output tile, 8 waves (two
-// per SIMD) of 128 (n) x 64 (m), K stepped 128 bytes at a time through two
-// swizzled LDS stages of 64 KB. Registers hold the next step's tiles; each
-// of the first two quarters of a step writes half of them to the other stage
-// and reloads that half two steps ahead. Requires K % 16 == 0.
-template <int DT, bool OV>
+// Large-tile forward kernel: 256 (m) x BN (n) output tile (BN = 256, or 128
+// when 256-wide tiles would leave compute units idle), 8 waves (two per SIMD)
+// of BN / 2 (n) x 64 (m), K stepped 128 bytes at a time through two swizzled
+// LDS stages of (256 + BN) x 128 bytes. Registers hold the next step's tiles;
+// each of the first two quarters of a step writes half of them to the other
+// stage and reloads that half two steps ahead. Requires K % 16 == 0.
+template <int DT, bool OV, int BN = 256>
 __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict__ CA,
                                                         const float* __restrict__ SCA, int M,
                                                         const int8_t* __restrict__ CB,
@@ -352,9 +355,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
                                                         const typename Elem<DT>::T* __restrict__ bias,
                                                         typename Elem<DT>::T* __restrict__ out,
                                                         int32_t* __restrict__ c32) {
-  constexpr int BM = 256, BN = 256, BK = 128, TI = 4, TJ = 2;
+  static_assert(BN == 256 || BN == 128, "256- or 128-wide tiles");
+  constexpr int BM = 256, BK = 128, TI = BN / 64, TJ = 2;
+  constexpr int NB = BN / 64;                  // register slots of the B tile
   constexpr int STAGE = (BM + BN) * BK;        // bytes per LDS stage
   constexpr int AOFF = BN * BK;                // A tile after the B tile
+  constexpr int OT = 256 * 512;                // the LDS output tile (rows of 256 16-bit values)
+  constexpr int BASE = 2 * STAGE > OT ? 2 * STAGE : OT;   // panels and scales after both
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -370,7 +377,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(CA + (int64_t)m0 * K, min(BM, M - m0) * K);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(CB + (int64_t)n0 * K, min(BN, N - n0) * K);
 
-  // global -> register slots: chunk lc (16 bytes) of rows lrow + 64 i, i < 4
+  // global -> register slots: chunk lc (16 bytes) of rows lrow + 64 i (i < NB
+  // for the B tile, i < 4 for the A tile)
   const int lrow = tid >> 3, lc = tid & 7;
   const int voff = lrow * K + 16 * lc;
   const int woff = lrow * BK + 16 * (lc ^ lds_swz(lrow));
@@ -378,14 +386,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   int roff[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) roff[ks] = lr * BK + 16 * ((2 * ks + lg) ^ sw);
-  const int pb = wn * 128 * BK, qb = AOFF + wm * 64 * BK;
+  const int pb = wn * (BN / 2) * BK, qb = AOFF + wm * 64 * BK;
 
-  v4u RB[4], RA[4];
+  v4u RB[NB], RA[4];
   // chunks past K (contraction tail) must read as zero: out of range
   auto load_b = [&](int kt) {
     const int v = (kt + 16 * lc < K) ? voff : OOB_OFFSET;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NB; ++i)
       RB[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rB, v, kt + 64 * i * K, 0));
   };
   auto load_a = [&](int kt) {
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   };
   auto write_b = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(smem + st * STAGE + woff + i * 64 * BK) = RB[i];
+    for (int i = 0; i < NB; ++i) *reinterpret_cast<v4u*>(smem + st * STAGE + woff + i * 64 * BK) = RB[i];
   };
   auto write_a = [&](int st) {
 #pragma unroll
@@ -432,7 +440,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   // outlier panels (first 16 outlier columns) for the epilogue, gathered while
   // the first operand tiles are in flight: thread t covers row t >> 1 of the
   // tile, columns 8 (t & 1) .. +7, of both panels
-  char* opan = reinterpret_cast<char*>(smem) + 2 * STAGE;
+  char* opan = reinterpret_cast<char*>(smem) + BASE;
   int o16 = 0;
   if (count != nullptr) o16 = min(min(*count, cap), 16);
   const int orow = tid >> 1, oj = (tid & 1) * 8;
@@ -441,7 +449,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   float psc = 0.0f;
   if (o16 > 0) {
     const int n = n0 + orow, m = m0 + orow;
-    const bool nok = n < N, mok = m < M;
+    const bool nok = (BN == 256 || orow < BN) && n < N, mok = m < M;
     psc = nok ? SCB[n] : 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   float sc0 = 0.0f, bias0 = 0.0f;
   if (tid < 256) {
     const int n = n0 + tid;
-    if (n < N) {
+    if ((BN == 256 || tid < BN) && n < N) {
       sc0 = SCB[n];
       if (bias != nullptr) bias0 = Elem<DT>::to_f32(bias[n]);
     }
@@ -489,6 +497,37 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   }
   __syncthreads();
   fread(0, 0, 0);
+  // instruction interleave inside a phase: each MFMA paired with a fragment
+  // read of the next phase and, in the first two phases, with an LDS tile
+  // write and a global load
+  auto groups_w = [&](auto nwr) {
+    constexpr int W = decltype(nwr)::value;
+    if constexpr (BN == 256) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        I8L_SGB(SG_MFMA, 1);
+        I8L_SGB(SG_DS_R, 1);
+        I8L_SGB(SG_DS_W, 1);
+        I8L_SGB(SG_VMEM_R, 1);
+      }
+      I8L_SGB(SG_MFMA, 1);
+      I8L_SGB(SG_DS_R, 2);
+      I8L_SGB(SG_MFMA, 3);
+    } else {
+#pragma unroll
+      for (int q = 0; q < W; ++q) {
+        I8L_SGB(SG_MFMA, 1);
+        I8L_SGB(SG_DS_R, 1);
+        I8L_SGB(SG_DS_W, 1);
+        I8L_SGB(SG_VMEM_R, 1);
+      }
+#pragma unroll
+      for (int q = W; q < TI * TJ; ++q) {
+        I8L_SGB(SG_MFMA, 1);
+        I8L_SGB(SG_DS_R, 1);
+      }
+    }
+  };
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     const int k2 = (kt + 2) * BK;    // past the end: zeros
@@ -496,40 +535,30 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
     write_b(st ^ 1);
     load_b(k2);
     mma(0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-      I8L_SGB(SG_DS_W, 1);
-      I8L_SGB(SG_VMEM_R, 1);
-    }
-    I8L_SGB(SG_MFMA, 1);
-    I8L_SGB(SG_DS_R, 2);
-    I8L_SGB(SG_MFMA, 3);
+    groups_w(std::integral_constant<int, NB>{});
     __builtin_amdgcn_sched_barrier(0);
     fread(st, 2, 0);
     write_a(st ^ 1);
     load_a(k2);
     mma(1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
-      I8L_SGB(SG_DS_W, 1);
-      I8L_SGB(SG_VMEM_R, 1);
-    }
-    I8L_SGB(SG_MFMA, 1);
-    I8L_SGB(SG_DS_R, 2);
-    I8L_SGB(SG_MFMA, 3);
+    groups_w(std::integral_constant<int, 4>{});
     __builtin_amdgcn_sched_barrier(0);
     fread(st, 3, 1);
     mma(0);
+    if constexpr (BN == 256) {
 #pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      I8L_SGB(SG_MFMA, 1);
-      I8L_SGB(SG_DS_R, 1);
+      for (int q = 0; q < 6; ++q) {
+        I8L_SGB(SG_MFMA, 1);
+        I8L_SGB(SG_DS_R, 1);
+      }
+      I8L_SGB(SG_MFMA, 2);
+    } else {
+#pragma unroll
+      for (int q = 0; q < TI * TJ; ++q) {
+        I8L_SGB(SG_MFMA, 1);
+        I8L_SGB(SG_DS_R, 1);
+      }
     }
-    I8L_SGB(SG_MFMA, 2);
     __builtin_amdgcn_sched_barrier(0);
     mma(1);
     __syncthreads();
@@ -538,31 +567,33 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
 
   const char* op = o16 > 0 ? opan : nullptr;
   if constexpr (DT == DT_F32) {
-    fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 64, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, idx,
-                                 count, bias, out, c32, nullptr, m0, n0, op, lsc);
+    fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 64, n0 + wn * (BN / 2), lr, lg, M, N, K, SCA, CB, SCB, subA, cap,
+                                 idx, count, bias, out, c32, nullptr, m0, n0, op, lsc);
   } else {
-    // output tile through LDS, stored as whole rows
+    // output tile through LDS, stored as whole rows (of the tile's BN columns)
     char* ot = reinterpret_cast<char*>(smem);
-    fwd_epilogue<TI, TJ, DT, OV, true>(acc, m0 + wm * 64, n0 + wn * 128, lr, lg, M, N, K, SCA, CB, SCB, subA, cap,
-                                       idx, count, bias, out, c32, ot, m0, n0, op, lsc);
+    fwd_epilogue<TI, TJ, DT, OV, true>(acc, m0 + wm * 64, n0 + wn * (BN / 2), lr, lg, M, N, K, SCA, CB, SCB, subA,
+                                       cap, idx, count, bias, out, c32, ot, m0, n0, op, lsc);
     __syncthreads();
-    otile_store<typename Elem<DT>::T>(ot, out, N, m0, n0, M, N, wave, lane);
+    otile_store<typename Elem<DT>::T>(ot, out, N, m0, n0, M, BN == 256 ? N : min(N, n0 + BN), wave, lane);
   }
 }
 
-template <int DT, bool OV>
+template <int DT, bool OV, int BN>
 static hipError_t launch_fwd_w8(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
                                 int N, int K, const uint16_t* subA, int cap, const int32_t* idx,
                                 const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   typedef typename Elem<DT>::T T;
-  constexpr size_t lds = (size_t)2 * (256 + 256) * 128 + OPAN_BYTES + LSC_BYTES;   // stages, panels, scales
-  auto kern = k_gemm_fwd_w8<DT, OV>;
+  // both stages (or the output tile, if larger), panels, scales
+  constexpr size_t stages = (size_t)2 * (256 + BN) * 128, otile = (size_t)256 * 512;
+  constexpr size_t lds = (stages > otile ? stages : otile) + OPAN_BYTES + LSC_BYTES;
+  auto kern = k_gemm_fwd_w8<DT, OV, BN>;
   static std::atomic<uint64_t> lds_set{0};
   {
     const hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
   }
-  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int tiles = ((M + 255) / 256) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count,
                      static_cast<const T*>(bias), static_cast<T*>(out), c32);
   return hipGetLastError();
@@ -593,9 +624,12 @@ static hipError_t launch_fwd_dt(const int8_t* CA, const float* SCA, int M, const
                                 const void* bias, void* out, int32_t* c32, hipStream_t st) {
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   if constexpr (KV) {
-    if (big_tiles >= 64) {
-      return launch_fwd_w8<DT, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st);
-    }
+    // 64 to 128 tiles of 256 x 256 would fill at most half of the 256 compute
+    // units: half-width tiles take about half the time each and fill them all
+    if (big_tiles >= 64 && big_tiles <= 128)
+      return launch_fwd_w8<DT, OV, 128>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st);
+    if (big_tiles > 128)
+      return launch_fwd_w8<DT, OV, 256>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st);
   }
   return launch_fwd_cfg<128, 128, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32,
                                                   st);

@@ -72,14 +72,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(const typename Elem<DT>::
   for (int j = 0; j < TJ; ++j) qoff[j] = GOFF + tr_off(wn * 2 + j);
 
   v4u RA[4], RG[4];
-  auto load_a = [&](int mc) {
+  // halves h = 0, 1 of the staging slots (row chunks p = 2h, 2h + 1)
+  auto load_a = [&](int mc, int h) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int p = 2 * h; p < 2 * h + 2; ++p)
       RA[p] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rA, avoff, (mc + 16 * p) * K * 2, 0));
   };
-  auto load_g = [&](int mc) {
+  auto load_g = [&](int mc, int h) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int p = 2 * h; p < 2 * h + 2; ++p)
       RG[p] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rG, gvoff, (mc + 16 * p) * N * 2, 0));
   };
   auto to_f16 = [&](v4u v) {
@@ -89,13 +90,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(const typename Elem<DT>::
     }
     return v;
   };
-  auto write_a = [&](int st) {
+  auto write_a = [&](int st, int h) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) *reinterpret_cast<v4u*>(wsm + st * STAGE + woff + p * 16 * ROWB) = to_f16(RA[p]);
+    for (int p = 2 * h; p < 2 * h + 2; ++p) *reinterpret_cast<v4u*>(wsm + st * STAGE + woff + p * 16 * ROWB) = to_f16(RA[p]);
   };
-  auto write_g = [&](int st) {
+  auto write_g = [&](int st, int h) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int p = 2 * h; p < 2 * h + 2; ++p)
       *reinterpret_cast<v4u*>(wsm + st * STAGE + GOFF + woff + p * 16 * ROWB) = to_f16(RG[p]);
   };
 
@@ -128,31 +129,44 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(const typename Elem<DT>::
   };
 
   const int nn = (M + BMC - 1) / BMC;
-  load_a(0);
-  load_g(0);
-  write_a(0);
-  write_g(0);
-  load_a(BMC);
-  load_g(BMC);
+  for (int h = 0; h < 2; ++h) {
+    load_a(0, h);
+    load_g(0, h);
+  }
+  for (int h = 0; h < 2; ++h) {
+    write_a(0, h);
+    write_g(0, h);
+  }
+  for (int h = 0; h < 2; ++h) {
+    load_a(BMC, h);
+    load_g(BMC, h);
+  }
   __syncthreads();
   fread(0, 0, 0);
+  // each phase of a step writes a quarter of the next stage: LDS writes run at
+  // about a third of the read rate, and spread evenly they cost less (2 %)
   for (int t = 0; t < nn; ++t) {
     const int st = t & 1;
     const int mc2 = (t + 2) * BMC;   // past the end: zeros
     fread(st, 1, 1);
-    write_a(st ^ 1);
-    load_a(mc2);
+    write_a(st ^ 1, 0);
+    load_a(mc2, 0);
     mma(0);
     __builtin_amdgcn_sched_barrier(0);
     fread(st, 2, 0);
-    write_g(st ^ 1);
-    load_g(mc2);
+    write_a(st ^ 1, 1);
+    load_a(mc2, 1);
     mma(1);
     __builtin_amdgcn_sched_barrier(0);
     fread(st, 3, 1);
+    write_g(st ^ 1, 0);
+    load_g(mc2, 0);
     mma(0);
     __builtin_amdgcn_sched_barrier(0);
+    write_g(st ^ 1, 1);
+    load_g(mc2, 1);
     mma(1);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     fread(st ^ 1, 0, 0);
   }

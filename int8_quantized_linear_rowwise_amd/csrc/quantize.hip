@@ -18,7 +18,8 @@
 //   k_rowquant   second read of X. Every workgroup first ORs the slab words
 //                into the column mask and computes the per-word popcount
 //                prefix in LDS (a few KB from L2); workgroup 0 also writes the
-//                ascending outlier list and the count. Then one wave per row:
+//                ascending outlier list and the count. Then one wave (or, for
+//                rows wider than 4096 16-bit values, one workgroup) per row:
 //                absmax over non-outlier columns (on magnitude bits), s as an
 //                fp16 value, inv = 127 / s (IEEE division), codes =
 //                rint(fl32(x * inv)) (|code| <= 127 by construction), 0 on
@@ -32,7 +33,7 @@ namespace i8l {
 constexpr int CF_COLS = 64;          // columns per flags workgroup (8 lanes x 8 columns)
 constexpr int CF_MAX_SLABS = 16;     // row slabs of the flags pass
 constexpr int CF_SLAB_WORDS = 2048;  // slabs * words the row kernel ORs per workgroup (at most)
-constexpr int RQ_MAX_BLOCKS = 1024;  // row-kernel workgroups (four rows at a time each)
+constexpr int RQ_MAX_BLOCKS = 1024;  // row-kernel workgroups (four rows, or one row, at a time each)
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
@@ -274,10 +275,12 @@ __global__ __launch_bounds__(256) void k_colflags(const typename Elem<DT>::T* __
 // of the slab words, exclusive per-word popcount prefix, both in LDS;
 // workgroup 0 writes the ascending outlier list (first cap entries) and the
 // count. Then one wave per row, a wave walks rows row0, row0 + W, ... (W
-// waves in the grid). VEC rows (cols % 8 == 0, 16-byte aligned) are read with
-// 16-byte loads and written with 8-byte stores; with NCH > 0 a row of at most
-// 64 * NCH chunks stays in registers between the absmax and the quantization,
-// otherwise it streams twice through the cache.
+// waves in the grid); with WG one workgroup per row instead, walking rows
+// blockIdx.x, blockIdx.x + gridDim.x, ... VEC rows (cols % 8 == 0, 16-byte
+// aligned) are read with 16-byte loads and written with 8-byte stores; with
+// NCH > 0 a row of at most NCH chunks per thread (64 NCH, or 256 NCH with WG)
+// stays in registers between the absmax and the quantization, so it is read
+// once; otherwise it streams twice through the cache.
 //
 // Quantization of one element: x16 = fp16(x), p = fl32(x16 * inv),
 // code = rint(p). For a non-outlier column |x16| <= s, and fl32(s * fl32(127 /
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(256) void k_colflags(const typename Elem<DT>::T* __
 // [-127, 127] never applies. rint is computed as fl32(p + 1.5 * 2^23), whose
 // low byte is the two's-complement code; contraction into an FMA is off so
 // that the product is rounded to fp32 first.
-template <int DT, int NCH, bool VEC>
+template <int DT, int NCH, bool VEC, bool WG = false>
 __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __restrict__ X, int64_t rows,
                                                   int cols, int tau_on, const uint32_t* __restrict__ bits,
                                                   int slabs, int8_t* __restrict__ codes, float* __restrict__ scale,
@@ -298,10 +301,12 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
   const int nwords = (cols + 31) >> 5;
   uint32_t* smask = smem_q;
   int32_t* sprefix = reinterpret_cast<int32_t*>(smem_q + nwords);
-  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-
-  const int64_t wstride = (int64_t)gridDim.x * 4;
-  const int64_t row0 = (int64_t)blockIdx.x * 4 + wid;
+  const int t = threadIdx.x, lane = t & 63, wid = __builtin_amdgcn_readfirstlane(t >> 6);
+  // a row belongs to one wave, or with WG to the whole workgroup (TPR threads)
+  constexpr int TPR = WG ? 256 : 64;
+  const int me = WG ? t : lane;
+  const int64_t wstride = WG ? (int64_t)gridDim.x : (int64_t)gridDim.x * 4;
+  const int64_t row0 = WG ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * 4 + wid;
   const int nchunk = (cols + 7) >> 3;
   auto load = [&](const T* xr, int ci, v4u& a, v4u& b) {
     if constexpr (VEC) {
@@ -321,18 +326,22 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
   }
   // the first row of a register-resident wave is requested before the
   // prologue, so that its memory latency overlaps the mask construction
+  // register-resident rows (16-bit, VEC) are read through a buffer resource
+  // per row: chunks past the row read as zero without a memory access, so the
+  // loads need no branch. The first row is requested before the prologue, so
+  // that its memory latency overlaps the mask construction.
   constexpr int NR = NCH > 0 ? NCH : 1;
-  v4u ra[NR], rb[NR];
-  if constexpr (NCH > 0) {
-    if (row0 < rows) {
-      const T* xr = X + row0 * (int64_t)cols;
+  v4u ra[NR], rb[NR] = {};
+  auto load_row = [&](int64_t r, v4u(&a)[NR]) {
+    const bool in = r < rows;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + (in ? r : 0) * (int64_t)cols, in ? cols * (int)sizeof(T) : 0);
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int ci = i * 64 + lane;
-        if (ci < nchunk) load(xr, ci, ra[i], rb[i]);
-      }
+    for (int i = 0; i < NR; ++i) {
+      const int ci = i * TPR + me;
+      a[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, ci < nchunk ? ci * 16 : OOB_OFFSET, 0, 0));
     }
-  }
+  };
+  if constexpr (NCH > 0) load_row(row0, ra);
 
   if (tau_on) {
     if (w0ok) {
@@ -481,8 +490,18 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
         if (c0 + e < cols) cr[e] = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xffu);
     }
   };
+  // with WG the wave maxima meet in LDS; the two slots alternate by row, so
+  // one barrier per row suffices
+  __shared__ uint32_t red[2][4];
+  int par = 0;
   auto finish = [&](uint32_t mx, float& s, float& inv) {
     mx = wave_umax(mx);
+    if constexpr (WG) {
+      if (lane == 0) red[par][wid] = mx;
+      __syncthreads();
+      mx = max(max(red[par][0], red[par][1]), max(red[par][2], red[par][3]));
+      par ^= 1;
+    }
     s = mag_to_half_value<DT>(mx);        // max |fp16(x)| = fp16 cast of the max magnitude
     inv = (s > 0.0f) ? (127.0f / s) : 0.0f;
   };
@@ -494,40 +513,34 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
   if constexpr (NCH > 0) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ci = i * 64 + lane;
+      const int ci = i * TPR + me;
       const uint32_t om = ci < nchunk ? chunk_mask(ci) : 0u;
       if (__builtin_amdgcn_ballot_w64(om != 0u) != 0) anyb |= 1u << i;
     }
   }
   auto rmask = [&](int i) -> uint32_t {
-    const int ci = i * 64 + lane;
+    const int ci = i * TPR + me;
     return ((anyb >> i) & 1u) && ci < nchunk ? chunk_mask(ci) : 0u;
   };
 
   if constexpr (NCH > 0) {
+    static_assert(VEC && DT != DT_F32, "register-resident rows are 16-bit, 16-byte aligned");
     for (int64_t row = row0; row < rows; row += wstride) {
-      if (row != row0) {
-        const T* xr = X + row * (int64_t)cols;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const int ci = i * 64 + lane;
-          if (ci < nchunk) load(xr, ci, ra[i], rb[i]);
-        }
-      }
+      if (row != row0) load_row(row, ra);
       uint32_t mx = 0u;
       float sv, inv;
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const int ci = i * 64 + lane;
+        const int ci = i * TPR + me;
         if (ci < nchunk) mx = max(mx, absmax(ra[i], rb[i], rmask(i), (anyb >> i) & 1u));
       }
       finish(mx, sv, inv);
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const int ci = i * 64 + lane;
+        const int ci = i * TPR + me;
         if (ci < nchunk) emit(row, ci, ra[i], rb[i], inv, rmask(i), (anyb >> i) & 1u);
       }
-      if (lane == 0) scale[row] = sv;
+      if (me == 0) scale[row] = sv;
     }
   } else {
     for (int64_t row = row0; row < rows; row += wstride) {
@@ -601,33 +614,45 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
   }
   const uint32_t* bits = preflags != nullptr ? preflags : scratch;
   // the row kernel also writes the outlier list and count (count 0 when the split is off)
-  const int64_t rblocks = rows > 0 ? (rows + 3) / 4 : 1;
-  dim3 grid((unsigned)(rblocks < RQ_MAX_BLOCKS ? rblocks : RQ_MAX_BLOCKS));
+  // workgroups: four rows at a time (one per wave), or one row at a time
+  const int64_t rblocks = rows > 0 ? ((rows + 3) / 4 < RQ_MAX_BLOCKS ? (rows + 3) / 4 : RQ_MAX_BLOCKS) : 1;
+  const int64_t wblocks = rows > 0 ? (rows < RQ_MAX_BLOCKS ? rows : RQ_MAX_BLOCKS) : 1;
   const int nchunk = (cols + 7) / 8;
   const size_t lds = tau_on ? (size_t)2 * (nwords > 0 ? nwords : 1) * 4 : 0;
-  // mask + prefix of the widest rows (I8L_MAX_COLS) take 64 KB of LDS
-#define I8L_RQ(NCH, VEC)                                                                                        \
+#define I8L_RQ(NCH, VEC, WGM)                                                                                   \
   do {                                                                                                          \
-    auto kern = k_rowquant<DT, NCH, VEC>;                                                                       \
+    auto kern = k_rowquant<DT, NCH, VEC, WGM>;                                                                  \
     if (lds > 32768) {                                                                                          \
       hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (e != hipSuccess) return e;                                                                            \
     }                                                                                                           \
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, X, rows, cols, (int)tau_on, bits, slabs, codes, scale,     \
-                       idx, count, sub, cap);                                                                   \
+    const int64_t nb = WGM ? wblocks : rblocks;                                                                 \
+    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(256), lds, st, X, rows, cols, (int)tau_on, bits, slabs,   \
+                       codes, scale, idx, count, sub, cap);                                                     \
   } while (0)
-  // rows of up to 4096 16-bit values stay in registers; fp32, wider, unaligned
-  // or ragged rows use the streaming path (fewer registers)
+  // 16-bit rows stay in registers between the absmax and the quantization:
+  // rows of up to 4096 values in one wave, up to 32768 values spread over a
+  // workgroup (4, 8 or 16 chunks of 8 per thread); fp32, wider, unaligned or
+  // ragged rows stream through the cache twice
   bool done = false;
   if constexpr (DT != DT_F32) {
     if (vec && nchunk <= 64 * 8) {
-      I8L_RQ(8, true);
+      I8L_RQ(8, true, false);
+      done = true;
+    } else if (vec && nchunk <= 256 * 4) {
+      I8L_RQ(4, true, true);
+      done = true;
+    } else if (vec && nchunk <= 256 * 8) {
+      I8L_RQ(8, true, true);
+      done = true;
+    } else if (vec && nchunk <= 256 * 16) {
+      I8L_RQ(16, true, true);
       done = true;
     }
   }
   if (!done) {
-    if (vec) I8L_RQ(0, true);
-    else I8L_RQ(0, false);
+    if (vec) I8L_RQ(0, true, false);
+    else I8L_RQ(0, false, false);
   }
 #undef I8L_RQ
   return hipGetLastError();

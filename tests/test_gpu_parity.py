@@ -52,10 +52,11 @@ def _check_quant(I8, X, dt, tau, cap=None):
 
 
 # rows of up to 4096 16-bit values stay in a wave's registers (several rows per
-# wave past 4096 rows); wider, ragged or fp32 rows stream through the cache
-# twice
-QSHAPES = [(1, 1), (3, 7), (17, 70), (64, 4096), (4100, 2048), (129, 4104), (5, 8200), (4100, 4104),
-           (33, 11008), (3, 20000), (2, 40000), (600, 4), (600, 16), (1000, 64)]
+# wave past 4096 rows), rows of up to 32768 in a workgroup's (4, 8 or 16
+# chunks per thread; several rows per workgroup past 1024 rows); wider,
+# ragged or fp32 rows stream through the cache twice
+QSHAPES = [(1, 1), (3, 7), (17, 70), (64, 4096), (4100, 2048), (129, 4104), (4100, 4104), (5, 8200),
+           (1100, 8200), (33, 11008), (3, 20000), (1030, 16392), (2, 40000), (600, 4), (600, 16), (1000, 64)]
 
 
 @pytest.mark.parametrize("dt", DTS)
@@ -175,10 +176,13 @@ def test_backward_parity(I8, dt, M, K, N):
 
 
 # shapes with at least 64 output tiles of 256 x 256, which select the
-# large-tile pipelined kernels; ragged in every dimension (partial tiles and a
-# contraction tail that is not a multiple of the k step)
-BIG_FWD = [(2100, 1040, 2090), (2048, 4096, 2048), (1030, 528, 4100), (2304, 16, 2304)]
-BIG_BWD = [(2100, 2088, 1044), (2048, 2048, 2048), (2060, 1000, 4100), (2304, 8, 2304)]
+# large-tile pipelined kernels (with half-width tiles up to 128 such tiles);
+# ragged in every dimension (partial tiles and a contraction tail that is not
+# a multiple of the k step)
+BIG_FWD = [(2100, 1040, 2090), (2048, 4096, 2048), (1030, 528, 4100), (2304, 16, 2304), (2100, 1040, 4200),
+           (4100, 528, 2090)]
+BIG_BWD = [(2100, 2088, 1044), (2048, 2048, 2048), (2060, 1000, 4100), (2304, 8, 2304), (2100, 1000, 2092),
+           (4100, 1000, 2092)]
 
 
 @pytest.mark.parametrize("dt", DTS)

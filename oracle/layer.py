@@ -30,7 +30,8 @@ Sources (public web pages):
 Notation: X16 is the fp16 cast of X; fl32(.) one correctly rounded fp32
 operation; rint round-half-to-even; D the tensor's storage dtype.
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent (each also listed, with the same number,
+in the design notes; 16-22 there concern the workloads, not this module):
   1. outlier columns: |X16| > tau strictly, tau compared in fp32;
   2. tau <= 0, tau = +inf or NaN disables the split (no outlier columns);
   3. a column is an outlier column if any row of the flattened batch exceeds tau;
@@ -61,6 +62,10 @@ Readings where the pages are silent (each also listed in the design notes):
      linear's output as stored in D and rounded to D once; the kernel that
      produces A = D(SiLU(H)) may also hand over A's outlier columns, which
      are by definition those the quantizer would find in A (readings 1-3, 7).
+ 23. the quantizer's domain is inputs whose fp16 cast is finite: the pages
+     cast to fp16 before quantizing, and a value beyond fp16's range (or a
+     non-finite input) has no int8 code; quantize_rowwise raises ValueError
+     for such inputs instead of producing one.
 
 Pins: tests/test_oracle_*.py (brute force with exact rationals, closed-form
 special cases, invariants, the pages' error bounds).
@@ -113,6 +118,10 @@ def quantize_rowwise(X: np.ndarray, dt: str, tau: float, chunk: int = 1024) -> d
     (int32 ascending), sub (float16, R x |O|).
     """
     X16 = to_half(X, dt)
+    if not np.all(np.isfinite(X16)):
+        # reading 23: the method's domain is inputs whose fp16 cast is finite
+        raise ValueError("quantize_rowwise: the fp16 cast of the input holds inf or NaN "
+                         "(|x| beyond 65504 after rounding, or a non-finite input)")
     R, C = X16.shape
     O = outlier_columns(X16, tau, chunk)
     keep = np.ones(C, dtype=bool)

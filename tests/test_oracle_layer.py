@@ -125,10 +125,12 @@ def _wl_rows(name, li, rows):
     return workloads.make_activation(wl, li, rows=rows), wl
 
 
-@pytest.mark.parametrize("name,li", [("single4096", 0), ("llama7b_mlp", 2), ("llama7b_block", 4),
-                                     ("mlp600", 0)])
-def test_quantizer_invariants(name, li):
-    A, wl = _wl_rows(name, li, 256 if name != "mlp600" else None)
+# rows: every row of single4096 (2048, two of the oracle's 1024-row chunks),
+# more than one chunk of the others
+@pytest.mark.parametrize("name,li,rows", [("single4096", 0, None), ("llama7b_mlp", 2, 1100),
+                                          ("llama7b_block", 4, 2048), ("mlp600", 0, None)])
+def test_quantizer_invariants(name, li, rows):
+    A, wl = _wl_rows(name, li, rows)
     dt, tau = wl.dtype, wl.threshold
     q = oracle.quantize_rowwise(A, dt, tau)
     X = to_half(A, dt).astype(np.float64)
@@ -584,3 +586,140 @@ def test_silu_activation_rounds_once(dt):
     a = to_f64(r["A"], dt)
     u = oracle.ulp(np.abs(r["y"]), dt)
     assert np.all(np.abs(a - r["y"]) <= 0.5 * u + 1e-300)
+
+
+# --------------------------------------------------------------------------
+# the oracle's row chunks (1024 rows bound its float64 temporaries): the
+# chunked loops must equal the plain definitions on inputs of several chunks
+
+
+def _chunk_case():
+    g = np.random.default_rng(60)
+    M, K, N = 1537, 72, 40
+    x = g.standard_normal((M, K)).astype(np.float32)
+    x[:, [5, 41]] *= 20                              # outlier columns spread over all rows
+    x[1536, 63] = 9.0                                # a column flagged only by the very last row
+    x[3, 17] = 7.5                                   # ... and one only by an early row
+    A = workloads._store(x, "bf16")
+    W = (g.standard_normal((N, K)) * 0.05).astype(np.float32)
+    G = workloads._store((g.standard_normal((M, N)) * 0.1).astype(np.float32), "bf16")
+    return A, W, G
+
+
+def test_chunked_loops_equal_plain_definition():
+    A, W, G = _chunk_case()
+    X16 = to_half(A, "bf16")
+    # plain definitions, no chunks
+    plain_O = np.nonzero((np.abs(X16.astype(np.float32)) > np.float32(6.0)).any(axis=0))[0]
+    assert plain_O.tolist() == [5, 17, 41, 63]
+    CB, SCB = oracle.quantize_weight(W)
+    for chunk in (7, 1024, 10 ** 9):
+        assert oracle.outlier_columns(X16, 6.0, chunk=chunk).tolist() == plain_O.tolist()
+    ref_q = oracle.quantize_rowwise(A, "bf16", 6.0, chunk=10 ** 9)
+    for chunk in (7, 1024):
+        q = oracle.quantize_rowwise(A, "bf16", 6.0, chunk=chunk)
+        assert q["outliers"].tolist() == plain_O.tolist()
+        assert np.array_equal(q["codes"], ref_q["codes"])
+        assert np.array_equal(q["scale"].view(np.uint32), ref_q["scale"].view(np.uint32))
+        assert np.array_equal(q["sub"].view(np.uint16), ref_q["sub"].view(np.uint16))
+    # the row scale of every row, written out per row without any chunking
+    keep = np.ones(X16.shape[1], bool)
+    keep[plain_O] = False
+    s_rows = np.array([np.abs(X16[r, keep].astype(np.float32)).max() for r in range(X16.shape[0])])
+    assert np.array_equal(ref_q["scale"], s_rows.astype(np.float32))
+    CA = ref_q["codes"]
+    ref_c = CA.astype(np.int64) @ CB.astype(np.int64).T          # textbook integer product
+    for chunk in (7, 1024, 10 ** 9):
+        assert np.array_equal(oracle.int_matmul(CA, CB, chunk=chunk), ref_c)
+    Wdq = oracle.dequant_weight(CB, SCB).astype(np.float64)
+    ref_b = to_half(G, "bf16").astype(np.float64) @ Wdq
+    for chunk in (7, 1024, 10 ** 9):
+        b = oracle.linear_backward_input(G, "bf16", CB, SCB, chunk=chunk)
+        assert np.array_equal(b["y"], ref_b)
+
+
+def test_quantizer_rejects_non_finite_half_cast():
+    """Reading 23: an input whose fp16 cast is not finite has no code."""
+    base = np.ones((3, 4), np.float32)
+    for bad in (70000.0, 65520.0, float("inf"), float("nan")):
+        x = base.copy()
+        x[1, 2] = bad
+        for dt in ("f32", "bf16"):
+            with pytest.raises(ValueError):
+                oracle.quantize_rowwise(workloads._store(x, dt) if dt == "bf16" else x, dt, 6.0)
+    x = base.copy()
+    x[1, 2] = 65504.0                                # the largest finite fp16 value is accepted
+    q = oracle.quantize_rowwise(x, "f32", 0.0)
+    assert q["codes"][1, 2] == 127 and q["scale"][1] == np.float32(65504.0)
+
+
+# --------------------------------------------------------------------------
+# the EasyDeL residual MLP's backward half, pinned against the float64
+# backward of the unquantized MLP (bitsandbytes PR #33 bounds)
+
+
+def _mlp600_case():
+    wl, Ws, bs = _mlp600_weights()
+    x = workloads.make_activation(wl, 0)
+    g = workloads.make_grad(wl, 1)
+    layers = []
+    for W, b in zip(Ws, bs):
+        cb, s = oracle.quantize_weight(W)
+        layers.append((cb, s, b))
+    r = oracle.mlp_forward_backward(x, g, "f32", layers, wl.threshold)
+    xf, gf = x.astype(np.float64), g.astype(np.float64)
+    W1, W2 = Ws[0].astype(np.float64), Ws[1].astype(np.float64)
+    b1 = bs[0].astype(np.float64) if bs[0] is not None else 0.0
+    b2 = bs[1].astype(np.float64) if bs[1] is not None else 0.0
+    h = xf @ W1.T + b1                               # unquantized float64 MLP
+    # derivative of SiLU by complex-step differentiation (no closed form of it)
+    hs = 1e-30
+    dsilu = np.imag((h + 1j * hs) / (1.0 + np.exp(-(h + 1j * hs)))) / hs
+    ref = {"h": h, "out": (h / (1.0 + np.exp(-h))) @ W2.T + b2 + xf}
+    ref["g_a"] = gf @ W2
+    ref["g_h"] = ref["g_a"] * dsilu
+    ref["grad_x"] = ref["g_h"] @ W1 + gf
+    ref["gb1"] = ref["g_h"].sum(axis=0)
+    ref["gb2"] = gf.sum(axis=0)
+    return r, ref, layers, (xf, gf, W1)
+
+
+def test_mlp600_backward_against_float_mlp():
+    r, ref, layers, (xf, gf, W1) = _mlp600_case()
+    for name in ("out", "grad_x", "gb1", "gb2"):
+        res = oracle.page_bounds(to_f64(r[name], "f32"), ref[name])
+        assert res["ok"], (name, res)
+    # two plausible slips in the composite backward break the grad_x bound:
+    # (1) SiLU' taken at the activation a instead of at the pre-activation h
+    g_a = to_f64(r["g_a"], "f32")
+    h = to_f64(r["h"], "f32")
+    cb1, s1, _ = layers[0]
+    slip1 = oracle.from_f64(g_a * oracle.silu_grad(to_f64(r["a"], "f32")), "f32")
+    gx1 = to_f64(oracle.linear_backward_input(slip1, "f32", cb1, s1)["grad_A"], "f32") + gf
+    assert not oracle.page_bounds(gx1, ref["grad_x"])["ok"]
+    assert not oracle.page_bounds(slip1.astype(np.float64).sum(axis=0), ref["gb1"])["ok"]
+    # (2) the residual's gradient + g dropped
+    gx2 = to_f64(oracle.linear_backward_input(r["g_h"], "f32", cb1, s1)["grad_A"], "f32")
+    assert not oracle.page_bounds(gx2, ref["grad_x"])["ok"]
+    # and the forward half without the residual input fails too
+    assert not oracle.page_bounds(to_f64(r["out"], "f32") - xf, ref["out"])["ok"]
+    # the un-slipped composition from the same pieces reproduces the oracle
+    gh = oracle.from_f64(g_a * oracle.silu_grad(h), "f32")
+    assert np.array_equal(gh, r["g_h"])
+
+
+def test_mlp600_g_h_is_silu_derivative_at_stored_h():
+    """g_h = D(g_a * SiLU'(h)) with h the first linear's stored output: SiLU'
+    by complex-step differentiation, elementwise within one unit of f32."""
+    r, ref, layers, _ = _mlp600_case()
+    h = to_f64(r["h"], "f32")
+    hs = 1e-30
+    d = np.imag((h + 1j * hs) / (1.0 + np.exp(-(h + 1j * hs)))) / hs
+    y = to_f64(r["g_a"], "f32") * d
+    from oracle.formats import ulp
+    err = np.abs(to_f64(r["g_h"], "f32") - y)
+    assert np.all(err <= 0.5 * ulp(np.abs(y), "f32") * (1 + 1e-6) + 1e-300)
+    # gb1 and gb2 are the column sums of g_h and g in f32 (one rounding of the exact sums)
+    assert np.array_equal(r["gb1"], oracle.from_f64(to_f64(r["g_h"], "f32").sum(axis=0), "f32"))
+    assert np.array_equal(r["gb2"], oracle.from_f64(to_f64(workloads.make_grad(workloads.WORKLOADS["mlp600"], 1),
+                                                           "f32").sum(axis=0), "f32"))

@@ -73,7 +73,8 @@ def make_gpu_inputs(wl, n_sets, seed_base=1234):
                            out=torch.empty((L.M, L.N), dtype=dt, device=dev),
                            gA=torch.empty((L.M, L.K), dtype=dt, device=dev),
                            gb=torch.empty((L.N,), dtype=dt, device=dev) if L.has_bias else None,
-                           wsf=I8.forward_workspace(L.M, L.K, L.K, dev),
+                           cap=I8.default_cap(L.K),
+                           wsf=I8.forward_workspace(L.M, L.K, I8.default_cap(L.K), dev),
                            wsb=torch.empty((max(1, I8.lib.int8_linear_backward_workspace_bytes(
                                L.M, L.N, int(L.has_bias))),), dtype=torch.uint8, device=dev)))
     torch.cuda.synchronize()
@@ -90,7 +91,7 @@ def run_gpu(wl, steps, warmup, n_sets, threshold):
 
     def call_fwd(ly, s):
         A, _ = ly["sets"][s]
-        I8.int8_linear_forward(A, ly["CB"], ly["SCB"], ly["bias"], threshold, ly["L"].K, out=ly["out"],
+        I8.int8_linear_forward(A, ly["CB"], ly["SCB"], ly["bias"], threshold, ly["cap"], out=ly["out"],
                                workspace=ly["wsf"])
 
     def call_bwd(ly, s):
@@ -103,9 +104,9 @@ def run_gpu(wl, steps, warmup, n_sets, threshold):
             call_fwd(ly, w % n_sets)
             call_bwd(ly, w % n_sets)
     torch.cuda.synchronize()
-    # outlier buffers never overflow (cap = K), checked once
-    for ly in layers:
-        I8.forward_check(ly["wsf"], ly["L"].M, ly["L"].K, ly["L"].K)
+    # outlier columns found by the forward (any number is handled; the first
+    # `cap` are staged, later ones read from the input by the epilogue)
+    n_outliers = [I8.forward_check(ly["wsf"], ly["L"].M, ly["L"].K, ly["cap"]) for ly in layers]
 
     # one step = forward of every layer (in order), then backward of every layer
     # (reverse order), as in a training step; one event pair brackets each phase
@@ -128,6 +129,7 @@ def run_gpu(wl, steps, warmup, n_sets, threshold):
     torch.cuda.synchronize()
     h1 = time.perf_counter()
     gpu_ms = ev[0][0].elapsed_time(ev[-1][2])
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
 
@@ -231,11 +233,11 @@ def run_gpu(wl, steps, warmup, n_sets, threshold):
         I8.silu_outlier_flags(Hs[s], threshold, A=As[s], flags=fls[s])
 
     def fwd_plain(s):
-        I8.int8_linear_forward(As[s], ly["CB"], ly["SCB"], ly["bias"], threshold, L.K, out=ly["out"],
+        I8.int8_linear_forward(As[s], ly["CB"], ly["SCB"], ly["bias"], threshold, ly["cap"], out=ly["out"],
                                workspace=ly["wsf"])
 
     def fwd_flagged(s):
-        I8.int8_linear_forward_flagged(As[s], fls[s], ly["CB"], ly["SCB"], ly["bias"], L.K, out=ly["out"],
+        I8.int8_linear_forward_flagged(As[s], fls[s], ly["CB"], ly["SCB"], ly["bias"], ly["cap"], out=ly["out"],
                                        workspace=ly["wsf"])
 
     def timed_leg(f, reps=10):
@@ -253,7 +255,7 @@ def run_gpu(wl, steps, warmup, n_sets, threshold):
               forward_flagged_ms=timed_leg(fwd_flagged))
     del As, fls
     return dict(layers=layers, gpu_ms=gpu_ms, host_s=h1 - h0, fwd_ms=fwd_ms, bwd_ms=bwd_ms, q_ms=q_ms,
-                bwd8_ms=bwd8_ms, wgrad_ms=wgrad_ms, pf=pf)
+                bwd8_ms=bwd8_ms, wgrad_ms=wgrad_ms, pf=pf, step_ms=step_ms, n_outliers=n_outliers)
 
 
 def copy_calibration(nbytes=1 << 30):
@@ -287,6 +289,44 @@ def traffic_from_profile(kernel_src: str, name: str):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def percentile(xs, p):
+    """p-th percentile (linear interpolation between order statistics)."""
+    v = sorted(xs)
+    if not v:
+        return None
+    x = (len(v) - 1) * p / 100.0
+    i = int(x)
+    j = min(i + 1, len(v) - 1)
+    return v[i] + (v[j] - v[i]) * (x - i)
+
+
+def combined_ceiling(wl, reads=2):
+    """The workload's best possible effective TOPS as a share of the int8
+    peak: every quantizer at full HBM bandwidth (its input read `reads` times:
+    2 for the two-pass quantizer used, 1 for the one-read minimum), every
+    forward GEMM at the int8 MFMA peak and every backward GEMM at the fp16
+    MFMA peak (its operands are fp16 by the method's definition)."""
+    isz = 4 if wl.dtype == "f32" else 2
+    ops = t = 0.0
+    for L in wl.layers:
+        q_bytes = reads * L.M * L.K * isz + L.M * L.K + 4 * L.M + L.K
+        t += q_bytes / (PEAK_HBM_GBS * 1e9) + 2 * L.M * L.N * L.K / (PEAK_INT8_TOPS * 1e12) \
+            + 2 * L.M * L.N * L.K / (PEAK_F16_TFLOPS * 1e12)
+        ops += 4 * L.M * L.N * L.K
+    return 100.0 * ops / t / 1e12 / PEAK_INT8_TOPS
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(wl, target_s, threshold):
@@ -336,6 +376,7 @@ def cpu_baseline(wl, target_s, threshold):
         Ms = max(64, (Ms // 64) * 64)
         ops, tt = timed(Ms)
     return {"value": ops / tt / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "host_cpu": host_cpu_model(), "host_threads_visible": len(os.sched_getaffinity(0)),
             "sample": f"all {len(wl.layers)} layers of {wl.name} at {Ms} tokens (of {Mmax}): quantize + "
                       f"forward + backward, numpy float64, {tt:.1f} s"}
 
@@ -386,6 +427,12 @@ def main():
                    "layers": ", ".join(f"{L.name} {L.K}->{L.N}" for L in wl.layers), "io_dtype": wl.dtype,
                    "threshold": threshold, "input_sets": args.sets},
         "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "ceiling_pct_int8_peak": round(combined_ceiling(wl, reads=2), 1),
+        "ceiling_pct_int8_peak_one_read": round(combined_ceiling(wl, reads=1), 1),
+        "step_ms": {"median": round(percentile(r["step_ms"], 50), 4), "p10": round(percentile(r["step_ms"], 10), 4),
+                    "p90": round(percentile(r["step_ms"], 90), 4), "min": round(min(r["step_ms"]), 4),
+                    "max": round(max(r["step_ms"]), 4)},
+        "outlier_columns_per_layer": r["n_outliers"],
         "roofline": {"kernel": "k_gemm_bwd_w8 (memory-efficient backward grad_A, fp16 MFMA)", "bound": "mfma",
                      "achieved": round(bwd_tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tflops / PEAK_F16_TFLOPS, 4),

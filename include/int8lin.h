@@ -60,7 +60,9 @@ enum {
   I8L_ESHAPE = -3,     /* size beyond what the kernels index, or K > I8L_MAX_K */
   I8L_EWORKSPACE = -4, /* workspace NULL or smaller than required */
   I8L_EHIP = -5,       /* a HIP launch or copy failed */
-  I8L_EOVERFLOW = -6   /* more outlier columns than the buffer capacity `cap` */
+  I8L_EOVERFLOW = -6   /* reserved: no call returns it (the forward handles any number of
+                          outlier columns; int8_quantize_rowwise reports |O| > cap
+                          through its count) */
 };
 
 /* Largest contraction length whose int32 accumulator cannot overflow:
@@ -107,17 +109,25 @@ int int8_quantize_rowwise(const void* X, int dtype, int64_t rows, int64_t cols, 
  *                 + bias[n])                                    (fp32 accumulate)
  * A: M x K of `dtype`; CB: N x K int8 row-major; SCB: N fp32; bias: N of
  * `dtype` or NULL; out: M x N of `dtype`; c32_debug: M x N int32 or NULL
- * (exports C32). cap: capacity of the outlier buffers inside the workspace
- * (cap >= K can never overflow). K <= I8L_MAX_K.
- * The workspace holds the quantized activation; its layout is reported by
- * int8_linear_forward_workspace_layout so that tests can read it back.
+ * (exports C32). K <= I8L_MAX_K.
+ * cap (>= 0): columns of the workspace's fp16 outlier sub-matrix subA. The
+ * values of the first cap outlier columns are staged there by the quantizer;
+ * the epilogue reads those of any further outlier column from A itself (the
+ * same fp16 cast), so every |O| <= K is handled and the output is complete
+ * for any cap. A small cap (a few times the expected |O|) keeps the
+ * workspace at about M*K + 2*M*cap bytes.
+ * The workspace holds the quantized activation (CA, SCA), the full outlier
+ * list (K entries), subA and the quantizer's flag words; its layout is
+ * reported by int8_linear_forward_workspace_layout so that tests can read it
+ * back. A must stay unchanged until the call has run (it is read twice by the
+ * quantizer and again by the epilogue).
  * ------------------------------------------------------------------------ */
 typedef struct {
   size_t count;   /* int32 |O| */
-  size_t idx;     /* int32[cap] outlier columns */
+  size_t idx;     /* int32[K] outlier columns, ascending (first |O| valid) */
   size_t scale;   /* fp32[M] SCA */
   size_t codes;   /* int8[M*K] CA */
-  size_t sub;     /* fp16[M*cap] subA */
+  size_t sub;     /* fp16[M*cap] subA: A16[:, O[j]] for j < min(|O|, cap) */
   size_t total;   /* bytes required */
 } i8l_forward_layout;
 
@@ -165,11 +175,25 @@ int int8_linear_forward_flagged(const void* A, int dtype, int64_t M, int64_t K, 
                                 int32_t cap, void* out, int32_t* c32_debug, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
-/* Synchronises `stream`, reads the outlier count of the last forward that used
- * `workspace` and returns I8L_EOVERFLOW if it exceeded `cap` (the output of
- * that call is then incomplete), else I8L_OK. *count receives |O| if non-NULL. */
+/* Synchronises `stream` and reads the outlier count |O| of the last forward
+ * that used `workspace` (laid out for M, K, cap) into *count (if non-NULL).
+ * Returns I8L_OK, or I8L_EINVAL / I8L_EHIP. The forward's output is complete
+ * for every count, so this call is a diagnostic, not a required check. */
 int int8_linear_forward_check(const void* workspace, int64_t M, int64_t K, int32_t cap, void* stream,
                               int32_t* count);
+
+/* Which GEMM kernel a call of this shape launches, for operands with the
+ * alignment of device allocations (host only: no HIP call, no device
+ * memory). int8_linear_forward_plan(dtype, M, K, N) for the forward product
+ * (also the int8 backward's, with K and N exchanged) and
+ * int8_linear_backward_plan(dtype, M, N, K) for the input gradient:
+ * 0 nothing to compute (empty output), 1 the generic 128 x 128 tile kernel,
+ * 2 the large pipelined kernel with 256 x 256 tiles, 3 the large kernel with
+ * 256 x 128 tiles (chosen where 256 x 256 tiles would fill at most half of the
+ * chip's 256 compute units). Negative: the error the call itself would
+ * return for these sizes or dtype. Used by tests to check the dispatch. */
+int int8_linear_forward_plan(int dtype, int64_t M, int64_t K, int64_t N);
+int int8_linear_backward_plan(int dtype, int64_t M, int64_t N, int64_t K);
 
 /* ------------------------------------------------------------------------ *
  * Memory-efficient backward, input gradient only (bitsandbytes PR #33, PR

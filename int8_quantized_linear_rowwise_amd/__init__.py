@@ -27,7 +27,7 @@ __all__ = [
     "int8_linear_backward_weight", "Int8LinearTrainableFunction", "Int8LinearTrainable",
     "outlier_flags_buffer", "silu_outlier_flags", "int8_linear_forward_flagged",
     "Int8LinearFunction", "Int8Linear", "Int8LinError", "forward_workspace", "forward_layout",
-    "forward_check", "DTYPE_CODE", "I8L_MAX_K",
+    "forward_check", "default_cap", "DTYPE_CODE", "I8L_MAX_K",
 ]
 
 DTYPE_CODE = {torch.float32: I8L_F32, torch.float16: I8L_F16, torch.bfloat16: I8L_BF16}
@@ -120,8 +120,19 @@ def forward_workspace(M: int, K: int, cap: int, device) -> torch.Tensor:
     return _empty((max(n, 1),), torch.uint8, device)
 
 
+DEFAULT_CAP = 256
+
+
+def default_cap(K: int) -> int:
+    """Columns of the forward workspace's fp16 outlier sub-matrix: the values
+    of further outlier columns are read from the input by the GEMM epilogue,
+    so this only sizes the staging buffer (the output is complete for any
+    number of outlier columns)."""
+    return min(int(K), DEFAULT_CAP)
+
+
 def forward_check(ws: torch.Tensor, M: int, K: int, cap: int) -> int:
-    """Synchronise and return the outlier count of the last forward on ws; raises on overflow."""
+    """Synchronise and return the outlier count |O| of the last forward on ws."""
     c = ctypes_int32()
     check(lib.int8_linear_forward_check(ws.data_ptr(), M, K, cap, _stream(ws.device), c),
           "int8_linear_forward")
@@ -139,6 +150,8 @@ def int8_linear_forward(A: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor, bi
     """out = A (int8-quantized) @ CB^T (dequantized) + outlier product + bias, in A's dtype.
 
     A: M x K; CB: N x K int8; SCB: N fp32; bias: N (A's dtype) or None.
+    cap: columns of the workspace's outlier staging (default min(K, 256));
+    any number of outlier columns is handled whatever its value.
     c32: optional M x N int32 tensor receiving the exact int8 product."""
     if A.dim() != 2 or CB.dim() != 2:
         raise ValueError("A and CB must be 2-D")
@@ -148,7 +161,7 @@ def int8_linear_forward(A: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor, bi
         raise ValueError("CB must be N x K int8 and SCB N fp32")
     if bias is not None and (bias.shape != (N,) or bias.dtype != A.dtype):
         raise ValueError("bias must have shape (N,) and A's dtype")
-    cap = K if cap is None else int(cap)
+    cap = default_cap(K) if cap is None else int(cap)
     _check_out(out, (M, N), A.dtype, "out")
     _check_out(c32, (M, N), torch.int32, "c32")
     if out is None:
@@ -204,7 +217,7 @@ def int8_linear_forward_flagged(A: torch.Tensor, flags: torch.Tensor, CB: torch.
         raise ValueError("bias must have shape (N,) and A's dtype")
     if flags.dtype != torch.int32 or flags.numel() < lib.int8_outlier_flags_words(M, K):
         raise ValueError("flags must be the int32 flag buffer of an M x K input")
-    cap = K if cap is None else int(cap)
+    cap = default_cap(K) if cap is None else int(cap)
     _check_out(out, (M, N), A.dtype, "out")
     _check_out(c32, (M, N), torch.int32, "c32")
     if out is None:

@@ -34,6 +34,8 @@ SIGNATURES = {
     "int8_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _f32, _i32, _vp, _vp, _vp, _sz,
                                    _vp]),
     "int8_linear_forward_check": (_int, [_vp, _i64, _i64, _i32, _vp, ctypes.POINTER(_i32)]),
+    "int8_linear_forward_plan": (_int, [_int, _i64, _i64, _i64]),
+    "int8_linear_backward_plan": (_int, [_int, _i64, _i64, _i64]),
     "int8_linear_backward_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "int8_linear_backward_input": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "int8_linear_backward_int8_workspace_bytes": (_sz, [_i64, _i64, _int]),

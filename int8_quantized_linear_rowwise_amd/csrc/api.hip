@@ -24,7 +24,8 @@ bool fwd_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* L) {
   L->count = off;
   off += ALIGN;
   L->idx = off;
-  off += align_up((size_t)(cap > 0 ? cap : 1) * 4);
+  // the outlier list holds every column that can be one: it never overflows
+  off += align_up((size_t)(K > 0 ? K : 1) * 4);
   L->scale = off;
   off += align_up((size_t)(M > 0 ? M : 1) * 4);
   L->codes = off;
@@ -114,11 +115,13 @@ static int forward_impl(const void* A, int dtype, int64_t M, int64_t K, const in
   uint16_t* subA = reinterpret_cast<uint16_t*>(w + L.sub);
   uint32_t* qscratch = reinterpret_cast<uint32_t*>(w + L.total - quant_scratch_bytes(M, K));
   hipStream_t st = (hipStream_t)stream;
+  // the first cap outlier columns are staged in subA; the epilogue reads the
+  // values of any further ones from A itself
   hipError_t e = i8l::launch_quantize(dtype, A, M, (int)K, threshold, CA, SCA, idx, count, subA, cap, qscratch, st,
-                                      preflags);
+                                      preflags, (int)K);
   if (e != hipSuccess) return I8L_EHIP;
-  e = i8l::launch_gemm_fwd(dtype, CA, SCA, (int)M, CB, SCB, (int)N, (int)K, subA, cap, idx, count, bias, out, c32,
-                           st);
+  e = i8l::launch_gemm_fwd(dtype, CA, SCA, (int)M, CB, SCB, (int)N, (int)K, subA, cap, A, idx, count, bias, out,
+                           c32, st);
   return hip_status(e);
 }
 
@@ -165,7 +168,21 @@ int int8_linear_forward_check(const void* ws, int64_t M, int64_t K, int32_t cap,
     return I8L_EHIP;
   if (hipStreamSynchronize(st) != hipSuccess) return I8L_EHIP;
   if (count) *count = c;
-  return c > cap ? I8L_EOVERFLOW : I8L_OK;
+  return I8L_OK;
+}
+
+int int8_linear_forward_plan(int dtype, int64_t M, int64_t K, int64_t N) {
+  if (!valid_dtype(dtype)) return I8L_EDTYPE;
+  if (M < 0 || K < 0 || N < 0) return I8L_EINVAL;
+  if (M > INT32_MAX || N > INT32_MAX || K > I8L_MAX_K) return I8L_ESHAPE;
+  return i8l::gemm_fwd_plan(dtype, M, N, K, true);
+}
+
+int int8_linear_backward_plan(int dtype, int64_t M, int64_t N, int64_t K) {
+  if (!valid_dtype(dtype)) return I8L_EDTYPE;
+  if (M < 0 || K < 0 || N < 0) return I8L_EINVAL;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return I8L_ESHAPE;
+  return i8l::gemm_bwd_plan(dtype, M, N, K, true);
 }
 
 size_t int8_linear_backward_workspace_bytes(int64_t M, int64_t N, int with_grad_bias) {
@@ -260,8 +277,8 @@ int int8_linear_backward_input_int8(const void* G, int dtype, int64_t M, int64_t
     // column-quantized weight copy: the forward kernel with K and N exchanged
     hipError_t e = i8l::launch_quantize(dtype, G, M, (int)N, 0.0f, CG, SG, nullptr, count, nullptr, 0, qscratch, st);
     if (e != hipSuccess) return I8L_EHIP;
-    e = i8l::launch_gemm_fwd(dtype, CG, SG, (int)M, CBt, SCBt, (int)K, (int)N, nullptr, 0, nullptr, count, nullptr,
-                             grad_A, c32_debug, st);
+    e = i8l::launch_gemm_fwd(dtype, CG, SG, (int)M, CBt, SCBt, (int)K, (int)N, nullptr, 0, nullptr, nullptr, count,
+                             nullptr, grad_A, c32_debug, st);
     if (e != hipSuccess) return I8L_EHIP;
   }
   if (grad_bias != nullptr && N > 0) {

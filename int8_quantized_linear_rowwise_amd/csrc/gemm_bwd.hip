@@ -263,7 +263,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_w8(const typename Elem<DT>:
   const int m0 = tm * BM, k0 = tk * BK;
 
   const __amdgpu_buffer_rsrc_t rG = make_rsrc(G + (int64_t)m0 * N, min(BM, M - m0) * N * 2);
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(CB + k0, N * K - k0);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(CB + k0, max(0, N * K - k0));
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(SCB, N * 4);
 
   // G slots: 16-byte chunk gc of rows grow + 64 i (i < 4)
@@ -467,23 +467,33 @@ static hipError_t launch_bwd_dt(const void* G, int M, int N, const int8_t* CB, c
   return launch_bwd_cfg<128, 128, 64, DT, GV, WV, OV>(G, M, N, CB, SCB, K, gA, st);
 }
 
+// The large-tile kernel needs 16-bit gradients, N % 8 == 0, K % 4 == 0, a
+// contraction (N > 0: its prologue reads two weight steps unconditionally)
+// and operands its 32-bit buffer offsets can address.
+int gemm_bwd_plan(int dt, int64_t M, int64_t N, int64_t K, bool aligned) {
+  if (M <= 0 || K <= 0) return 0;
+  const bool fits = (N + 128) * K < ((int64_t)1 << 31) - 4096 && N * 2 * 256 < ((int64_t)1 << 31) - 4096;
+  const int64_t big_tiles = ((M + 255) / 256) * ((K + 255) / 256);
+  if (dt != DT_F32 && aligned && N > 0 && N % 8 == 0 && K % 4 == 0 && fits && big_tiles >= 64) {
+    // 64 to 128 tiles of 256 x 256 would fill at most half of the 256 compute
+    // units: half-width tiles take about half the time each and fill them all
+    return big_tiles <= 128 ? 3 : 2;
+  }
+  return 1;
+}
+
 hipError_t launch_gemm_bwd(int dt, const void* G, int M, int N, const int8_t* CB, const float* SCB, int K,
                            void* gA, hipStream_t st) {
   const int esz = dt == DT_F32 ? 4 : 2;
   const bool gv = (N % 8 == 0) && ((uintptr_t)G % 16 == 0);
   const bool wv = (K % 4 == 0) && ((uintptr_t)CB % 4 == 0);
   const bool ov = (K % 4 == 0) && ((uintptr_t)gA % (4 * esz) == 0);
-  // the large-tile kernel addresses its operands with 32-bit buffer offsets
-  const bool fits = ((int64_t)N + 128) * K < ((int64_t)1 << 31) - 4096 &&
-                    (int64_t)N * 2 * 256 < ((int64_t)1 << 31) - 4096;
-  const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((K + 255) / 256);
-  if (dt != DT_F32 && gv && wv && ov && fits && big_tiles >= 64) {
-    // 64 to 128 tiles of 256 x 256 would fill at most half of the 256 compute
-    // units: half-width tiles take about half the time each and fill them all
-    if (big_tiles <= 128) {
-      if (dt == DT_F16) return launch_bwd_w8<DT_F16, true, 128>(G, M, N, CB, SCB, K, gA, st);
-      return launch_bwd_w8<DT_BF16, true, 128>(G, M, N, CB, SCB, K, gA, st);
-    }
+  const int plan = gemm_bwd_plan(dt, M, N, K, gv && wv && ov);
+  if (plan == 3) {
+    if (dt == DT_F16) return launch_bwd_w8<DT_F16, true, 128>(G, M, N, CB, SCB, K, gA, st);
+    return launch_bwd_w8<DT_BF16, true, 128>(G, M, N, CB, SCB, K, gA, st);
+  }
+  if (plan == 2) {
     if (dt == DT_F16) return launch_bwd_w8<DT_F16, true, 256>(G, M, N, CB, SCB, K, gA, st);
     return launch_bwd_w8<DT_BF16, true, 256>(G, M, N, CB, SCB, K, gA, st);
   }

@@ -3,7 +3,7 @@
 // bitsandbytes PR #33 "Memory efficient backward", review on _functions.py
 // (dequantize, cast, add bias; "4. Mixed-precision decomposition matmul"):
 //   y[m, n] = C32[m, n] * SCA[m] * SCB[n] / 127^2
-//             + sum_j subA[m, j] * Wdq[n, O[j]]       (fp16 x fp16 -> fp32)
+//             + sum_j A16[m, O[j]] * Wdq[n, O[j]]     (fp16 x fp16 -> fp32)
 //             + bias[n]
 //   out = D(y)
 // with C32 = CA . CB^T exact in int32, CA (M x K) and CB (N x K) both int8
@@ -30,7 +30,7 @@ namespace i8l {
 //
 // opan (optional): LDS panels of the first 16 outlier columns for a 256 x 256
 // block tile with origin (tm0, tn0): P[n][16] = Wdq[n, O[j]] at opan, then
-// Q[m][16] = subA[m, j] at opan + OPAN_Q (fp16, 32 bytes per row, zero past
+// Q[m][16] = A16[m, O[j]] at opan + OPAN_Q (fp16, 32 bytes per row, zero past
 // the count); filled by the kernel before its k loop.
 //
 // With LDS_OUT (16-bit outputs, eight waves over a 256 x 256 block tile whose
@@ -44,11 +44,24 @@ constexpr int OPAN_BYTES = 2 * 256 * 32;
 // before its k loop.
 constexpr int LSC_SCB = 0, LSC_SCA = 256, LSC_BIAS = 512, LSC_BYTES = 768 * 4;
 
+// fp16 bits of outlier value j of row m: the quantizer's staged copy for the
+// first cap columns, beyond them the fp16 cast of A[m, idx[j]] read from the
+// layer input itself (the same value, so any number of outlier columns is
+// handled without a staging buffer of K columns).
+template <int DT>
+__device__ __forceinline__ uint16_t outlier_half(const uint16_t* __restrict__ subA, int cap,
+                                                 const typename Elem<DT>::T* __restrict__ A, int K,
+                                                 const int32_t* __restrict__ idx, int m, int j) {
+  if (j < cap) return subA[(int64_t)m * cap + j];
+  return __builtin_bit_cast(uint16_t, to_half<DT>(A[(int64_t)m * K + idx[j]]));
+}
+
 template <int TI, int TJ, int DT, bool OV, bool LDS_OUT = false>
 __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw, int lr, int lg, int M, int N, int K,
                                              const float* __restrict__ SCA, const int8_t* __restrict__ CB,
                                              const float* __restrict__ SCB, const uint16_t* __restrict__ subA,
-                                             int cap, const int32_t* __restrict__ idx,
+                                             int cap, const typename Elem<DT>::T* __restrict__ Asrc,
+                                             const int32_t* __restrict__ idx,
                                              const int32_t* __restrict__ count,
                                              const typename Elem<DT>::T* __restrict__ bias,
                                              typename Elem<DT>::T* __restrict__ out, int32_t* __restrict__ c32,
@@ -90,11 +103,7 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
     if (lsc != nullptr) sa[j] = lsc[LSC_SCA + m - tm0];
     else sa[j] = (m < M) ? SCA[m] : 0.0f;
   }
-  int cnt = 0;
-  if (count != nullptr) {
-    cnt = *count;
-    if (cnt > cap) cnt = cap;
-  }
+  const int cnt = count != nullptr ? *count : 0;
 
   // one slab of TJ tiles (32 output features) at a time keeps the fp32 copy small
 #pragma unroll
@@ -167,11 +176,11 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
       for (int j = 0; j < TJ; ++j) {
         const int m = mw + j * 32 + lr;
         const bool mok = m < M;
-        const uint16_t* srow = subA + (int64_t)(mok ? m : 0) * cap;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int jj = jo + lg * 8 + e;
-          Q[j][e] = (mok && jj < cnt) ? __builtin_bit_cast(_Float16, srow[jj]) : (_Float16)0.0f;
+          Q[j][e] = (mok && jj < cnt) ? __builtin_bit_cast(_Float16, outlier_half<DT>(subA, cap, Asrc, K, idx, m, jj))
+                                      : (_Float16)0.0f;
         }
       }
 #pragma unroll
@@ -233,6 +242,7 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(const int8_t* __restrict__ CA,
                                                   int M, const int8_t* __restrict__ CB,
                                                   const float* __restrict__ SCB, int N, int K,
                                                   const uint16_t* __restrict__ subA, int cap,
+                                                  const typename Elem<DT>::T* __restrict__ Asrc,
                                                   const int32_t* __restrict__ idx,
                                                   const int32_t* __restrict__ count,
                                                   const typename Elem<DT>::T* __restrict__ bias,
@@ -334,8 +344,8 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(const int8_t* __restrict__ CA,
     __syncthreads();
   }
 
-  fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * WM, n0 + wn * WN, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, idx,
-                               count, bias, out, c32);
+  fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * WM, n0 + wn * WN, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, Asrc,
+                               idx, count, bias, out, c32);
 }
 
 // Large-tile forward kernel: 256 (m) x BN (n) output tile (BN = 256, or 128
@@ -350,6 +360,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
                                                         const int8_t* __restrict__ CB,
                                                         const float* __restrict__ SCB, int N, int K,
                                                         const uint16_t* __restrict__ subA, int cap,
+                                                        const typename Elem<DT>::T* __restrict__ Asrc,
                                                         const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ count,
                                                         const typename Elem<DT>::T* __restrict__ bias,
@@ -442,7 +453,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   // tile, columns 8 (t & 1) .. +7, of both panels
   char* opan = reinterpret_cast<char*>(smem) + BASE;
   int o16 = 0;
-  if (count != nullptr) o16 = min(min(*count, cap), 16);
+  if (count != nullptr) o16 = min(*count, 16);
   const int orow = tid >> 1, oj = (tid & 1) * 8;
   int pbyte[8];
   uint16_t qval[8];
@@ -455,7 +466,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
     for (int e = 0; e < 8; ++e) {
       const int j = oj + e;
       pbyte[e] = (nok && j < o16) ? (int)CB[(int64_t)n * K + idx[j]] : 0;
-      qval[e] = (mok && j < o16) ? subA[(int64_t)m * cap + j] : (uint16_t)0;
+      qval[e] = (mok && j < o16) ? outlier_half<DT>(subA, cap, Asrc, K, idx, m, j) : (uint16_t)0;
     }
   }
 
@@ -568,12 +579,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   const char* op = o16 > 0 ? opan : nullptr;
   if constexpr (DT == DT_F32) {
     fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 64, n0 + wn * (BN / 2), lr, lg, M, N, K, SCA, CB, SCB, subA, cap,
-                                 idx, count, bias, out, c32, nullptr, m0, n0, op, lsc);
+                                 Asrc, idx, count, bias, out, c32, nullptr, m0, n0, op, lsc);
   } else {
     // output tile through LDS, stored as whole rows (of the tile's BN columns)
     char* ot = reinterpret_cast<char*>(smem);
     fwd_epilogue<TI, TJ, DT, OV, true>(acc, m0 + wm * 64, n0 + wn * (BN / 2), lr, lg, M, N, K, SCA, CB, SCB, subA,
-                                       cap, idx, count, bias, out, c32, ot, m0, n0, op, lsc);
+                                       cap, Asrc, idx, count, bias, out, c32, ot, m0, n0, op, lsc);
     __syncthreads();
     otile_store<typename Elem<DT>::T>(ot, out, N, m0, n0, M, BN == 256 ? N : min(N, n0 + BN), wave, lane);
   }
@@ -581,7 +592,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
 
 template <int DT, bool OV, int BN>
 static hipError_t launch_fwd_w8(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                                int N, int K, const uint16_t* subA, int cap, const int32_t* idx,
+                                int N, int K, const uint16_t* subA, int cap, const void* A, const int32_t* idx,
                                 const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   typedef typename Elem<DT>::T T;
   // both stages (or the output tile, if larger), panels, scales
@@ -594,14 +605,14 @@ static hipError_t launch_fwd_w8(const int8_t* CA, const float* SCA, int M, const
     if (e != hipSuccess) return e;
   }
   const int tiles = ((M + 255) / 256) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count,
-                     static_cast<const T*>(bias), static_cast<T*>(out), c32);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap,
+                     static_cast<const T*>(A), idx, count, static_cast<const T*>(bias), static_cast<T*>(out), c32);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int BK, int DT, bool KV, bool OV>
 static hipError_t launch_fwd_cfg(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                                 int N, int K, const uint16_t* subA, int cap, const int32_t* idx,
+                                 int N, int K, const uint16_t* subA, int cap, const void* A, const int32_t* idx,
                                  const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   typedef typename Elem<DT>::T T;
   constexpr int LDK = BK + 16;
@@ -613,36 +624,47 @@ static hipError_t launch_fwd_cfg(const int8_t* CA, const float* SCA, int M, cons
     if (e != hipSuccess) return e;
   }
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count,
-                     static_cast<const T*>(bias), static_cast<T*>(out), c32);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap,
+                     static_cast<const T*>(A), idx, count, static_cast<const T*>(bias), static_cast<T*>(out), c32);
   return hipGetLastError();
+}
+
+int gemm_fwd_plan(int dt, int64_t M, int64_t N, int64_t K, bool aligned) {
+  (void)dt;
+  if (M <= 0 || N <= 0) return 0;
+  if (aligned && K % 16 == 0) {
+    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    // 64 to 128 tiles of 256 x 256 would fill at most half of the 256 compute
+    // units: half-width tiles take about half the time each and fill them all
+    if (big_tiles >= 64 && big_tiles <= 128) return 3;
+    if (big_tiles > 128) return 2;
+  }
+  return 1;
 }
 
 template <int DT, bool KV, bool OV>
 static hipError_t launch_fwd_dt(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                                int N, int K, const uint16_t* subA, int cap, const int32_t* idx, const int32_t* count,
-                                const void* bias, void* out, int32_t* c32, hipStream_t st) {
-  const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+                                int N, int K, const uint16_t* subA, int cap, const void* A, const int32_t* idx,
+                                const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
+  const int plan = gemm_fwd_plan(DT, M, N, K, KV);
   if constexpr (KV) {
-    // 64 to 128 tiles of 256 x 256 would fill at most half of the 256 compute
-    // units: half-width tiles take about half the time each and fill them all
-    if (big_tiles >= 64 && big_tiles <= 128)
-      return launch_fwd_w8<DT, OV, 128>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st);
-    if (big_tiles > 128)
-      return launch_fwd_w8<DT, OV, 256>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st);
+    if (plan == 3)
+      return launch_fwd_w8<DT, OV, 128>(CA, SCA, M, CB, SCB, N, K, subA, cap, A, idx, count, bias, out, c32, st);
+    if (plan == 2)
+      return launch_fwd_w8<DT, OV, 256>(CA, SCA, M, CB, SCB, N, K, subA, cap, A, idx, count, bias, out, c32, st);
   }
-  return launch_fwd_cfg<128, 128, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32,
-                                                  st);
+  return launch_fwd_cfg<128, 128, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, A, idx, count, bias, out,
+                                                  c32, st);
 }
 
 hipError_t launch_gemm_fwd(int dt, const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                           int N, int K, const uint16_t* subA, int cap, const int32_t* idx, const int32_t* count,
-                           const void* bias, void* out, int32_t* c32, hipStream_t st) {
+                           int N, int K, const uint16_t* subA, int cap, const void* Asrc, const int32_t* idx,
+                           const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   const bool kv = (K % 16 == 0) && ((uintptr_t)CA % 16 == 0) && ((uintptr_t)CB % 16 == 0);
   const int osz = dt == DT_F32 ? 4 : 2;
   const bool ov = (N % 4 == 0) && ((uintptr_t)out % (4 * osz) == 0) && (c32 == nullptr || (uintptr_t)c32 % 16 == 0);
 #define I8L_FWD(D, A, B) \
-  return launch_fwd_dt<D, A, B>(CA, SCA, M, CB, SCB, N, K, subA, cap, idx, count, bias, out, c32, st)
+  return launch_fwd_dt<D, A, B>(CA, SCA, M, CB, SCB, N, K, subA, cap, Asrc, idx, count, bias, out, c32, st)
   switch (dt) {
     case DT_F32:
       if (kv) { if (ov) I8L_FWD(DT_F32, true, true); else I8L_FWD(DT_F32, true, false); }

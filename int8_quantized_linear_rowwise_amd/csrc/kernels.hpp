@@ -7,14 +7,15 @@
 namespace i8l {
 
 // Quantizer: X (rows x cols, dtype dt) -> codes, scale, outlier list (first
-// `cap` entries), count, sub (rows x cap fp16). scratch: quant_scratch_words()
+// idx_cap entries; idx_cap < 0 means cap), count, sub (rows x cap fp16: the
+// values of the first cap outlier columns). scratch: quant_scratch_words()
 // 32-bit words.
 // preflags: column flag words ([slabs][words], the layout of the scratch)
 // handed over by the producer of X; the flags pass is then skipped.
 size_t quant_scratch_words(int64_t rows, int64_t cols);
 hipError_t launch_quantize(int dt, const void* X, int64_t rows, int cols, float tau, int8_t* codes, float* scale,
                            int32_t* idx, int32_t* count, uint16_t* sub, int cap, uint32_t* scratch,
-                           hipStream_t st, const uint32_t* preflags = nullptr);
+                           hipStream_t st, const uint32_t* preflags = nullptr, int idx_cap = -1);
 
 // Producer of a quantizer input: A = D(SiLU(H)) and A's column flag words
 // (quant_scratch_words(rows, cols) words) for tau.
@@ -22,10 +23,19 @@ hipError_t launch_silu_flags(int dt, const void* H, int64_t rows, int cols, floa
                              hipStream_t st);
 
 // Forward GEMM with fused epilogue: out = D(CA.CB^T * SCA SCB / 127^2
-// + subA . Wdq[:, idx]^T + bias); optional int32 export of CA.CB^T.
+// + A16[:, idx] . Wdq[:, idx]^T + bias); optional int32 export of CA.CB^T.
+// The outlier values of the first cap columns come from subA (M x cap fp16),
+// those of later columns straight from A (M x K of dt, fp16 cast on the fly);
+// idx holds all *count columns.
 hipError_t launch_gemm_fwd(int dt, const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                           int N, int K, const uint16_t* subA, int cap, const int32_t* idx, const int32_t* count,
-                           const void* bias, void* out, int32_t* c32, hipStream_t st);
+                           int N, int K, const uint16_t* subA, int cap, const void* A, const int32_t* idx,
+                           const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st);
+
+// Kernel chosen for a forward / backward GEMM of this shape (operands 16-byte
+// aligned): 0 none (empty output), 1 the generic 128 x 128 kernel, 2 the
+// large 256 x 256 tile kernel, 3 the large kernel with 256 x 128 tiles.
+int gemm_fwd_plan(int dt, int64_t M, int64_t N, int64_t K, bool aligned);
+int gemm_bwd_plan(int dt, int64_t M, int64_t N, int64_t K, bool aligned);
 
 // Backward-input GEMM: grad_A = D(fp16(G) . Wdq), Wdq built from CB on the fly.
 hipError_t launch_gemm_bwd(int dt, const void* G, int M, int N, const int8_t* CB, const float* SCB, int K,

@@ -274,7 +274,9 @@ __global__ __launch_bounds__(256) void k_colflags(const typename Elem<DT>::T* __
 // Row quantization. Prologue of every workgroup (tau on): column mask = OR
 // of the slab words, exclusive per-word popcount prefix, both in LDS;
 // workgroup 0 writes the ascending outlier list (first cap entries) and the
-// count. Then one wave per row, a wave walks rows row0, row0 + W, ... (W
+// count (the first idx_cap entries of the list; the outlier values of the
+// first cap columns go to the dense sub-matrix). Then one wave per row, a
+// wave walks rows row0, row0 + W, ... (W
 // waves in the grid); with WG one workgroup per row instead, walking rows
 // blockIdx.x, blockIdx.x + gridDim.x, ... VEC rows (cols % 8 == 0, 16-byte
 // aligned) are read with 16-byte loads and written with 8-byte stores; with
@@ -292,8 +294,8 @@ template <int DT, int NCH, bool VEC, bool WG = false>
 __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __restrict__ X, int64_t rows,
                                                   int cols, int tau_on, const uint32_t* __restrict__ bits,
                                                   int slabs, int8_t* __restrict__ codes, float* __restrict__ scale,
-                                                  int32_t* __restrict__ idx, int32_t* __restrict__ count,
-                                                  uint16_t* __restrict__ sub, int cap) {
+                                                  int32_t* __restrict__ idx, int idx_cap,
+                                                  int32_t* __restrict__ count, uint16_t* __restrict__ sub, int cap) {
 #pragma clang fp contract(off)
   typedef typename Elem<DT>::T T;
   extern __shared__ uint32_t smem_q[];
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
         int j = run;
         while (mw) {
           const int b = __ffs(mw) - 1;
-          if (j < cap) idx[j] = w * 32 + b;
+          if (j < idx_cap) idx[j] = w * 32 + b;
           ++j;
           mw &= mw - 1u;
         }
@@ -596,7 +598,7 @@ size_t quant_scratch_words(int64_t rows, int64_t cols) {
 
 template <int DT>
 static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, float tau, int8_t* codes,
-                                    float* scale, int32_t* idx, int32_t* count, uint16_t* sub, int cap,
+                                    float* scale, int32_t* idx, int idx_cap, int32_t* count, uint16_t* sub, int cap,
                                     uint32_t* scratch, const uint32_t* preflags, hipStream_t st) {
   typedef typename Elem<DT>::T T;
   const T* X = static_cast<const T*>(Xv);
@@ -628,7 +630,7 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
     }                                                                                                           \
     const int64_t nb = WGM ? wblocks : rblocks;                                                                 \
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(256), lds, st, X, rows, cols, (int)tau_on, bits, slabs,   \
-                       codes, scale, idx, count, sub, cap);                                                     \
+                       codes, scale, idx, idx_cap, count, sub, cap);                                            \
   } while (0)
   // 16-bit rows stay in registers between the absmax and the quantization:
   // rows of up to 4096 values in one wave, up to 32768 values spread over a
@@ -660,14 +662,18 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
 
 hipError_t launch_quantize(int dt, const void* X, int64_t rows, int cols, float tau, int8_t* codes, float* scale,
                            int32_t* idx, int32_t* count, uint16_t* sub, int cap, uint32_t* scratch,
-                           hipStream_t st, const uint32_t* preflags) {
+                           hipStream_t st, const uint32_t* preflags, int idx_cap) {
+  if (idx_cap < 0) idx_cap = cap;
   switch (dt) {
     case DT_F32:
-      return launch_quantize_t<DT_F32>(X, rows, cols, tau, codes, scale, idx, count, sub, cap, scratch, preflags, st);
+      return launch_quantize_t<DT_F32>(X, rows, cols, tau, codes, scale, idx, idx_cap, count, sub, cap, scratch,
+                                       preflags, st);
     case DT_F16:
-      return launch_quantize_t<DT_F16>(X, rows, cols, tau, codes, scale, idx, count, sub, cap, scratch, preflags, st);
+      return launch_quantize_t<DT_F16>(X, rows, cols, tau, codes, scale, idx, idx_cap, count, sub, cap, scratch,
+                                       preflags, st);
     default:
-      return launch_quantize_t<DT_BF16>(X, rows, cols, tau, codes, scale, idx, count, sub, cap, scratch, preflags, st);
+      return launch_quantize_t<DT_BF16>(X, rows, cols, tau, codes, scale, idx, idx_cap, count, sub, cap, scratch,
+                                        preflags, st);
   }
 }
 

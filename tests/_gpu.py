@@ -63,3 +63,13 @@ def assert_float_gate(T: np.ndarray, dt: str, y: np.ndarray, what: str, tight_ul
     bad = err > lim
     assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond the tight bound; worst "
                            f"{float((err / lim).max()):.3g}x at {np.unravel_index(np.argmax(err / lim), err.shape)}")
+
+
+def tile_rows(M: int, tile: int = 256, seed: int = 0) -> np.ndarray:
+    """Rows for sampled full-size checks: one random row inside every tile of
+    `tile` rows (so no row tile of the kernels goes unchecked), plus the first
+    and last rows and the rows around the first tile boundary."""
+    g = np.random.default_rng(seed)
+    r = {int(t + g.integers(0, min(tile, M - t))) for t in range(0, M, tile)}
+    r |= {x for x in (0, tile - 1, tile, tile + 1, M - 1) if 0 <= x < M}
+    return np.array(sorted(r), dtype=np.int64)

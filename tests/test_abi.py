@@ -231,12 +231,48 @@ def test_forward_layout(L):
         lay = L.ForwardLayout()
         assert L.lib.int8_linear_forward_workspace_layout(M, K, cap, lay) == 0
         offs = [lay.count, lay.idx, lay.scale, lay.codes, lay.sub]
-        sizes = [4, 4 * cap, 4 * M, M * K, 2 * M * cap]
+        sizes = [4, 4 * K, 4 * M, M * K, 2 * M * cap]
         assert all(o % 256 == 0 for o in offs)
         for (o, s), o2 in zip(zip(offs, sizes), offs[1:] + [lay.total]):
             assert o + s <= o2
         assert lay.total == L.lib.int8_linear_forward_workspace_bytes(M, K, cap)
     assert L.lib.int8_linear_forward_workspace_layout(-1, 4, 4, L.ForwardLayout()) == L.I8L_EINVAL
+    # the outlier list always has room for every column; only the staging width follows cap
+    small, big = L.ForwardLayout(), L.ForwardLayout()
+    L.lib.int8_linear_forward_workspace_layout(16384, 28672, 256, small)
+    L.lib.int8_linear_forward_workspace_layout(16384, 28672, 28672, big)
+    assert small.sub - small.idx >= 4 * 28672
+    assert small.total < 16384 * 28672 + 2 * 16384 * 256 + (1 << 20)
+    assert big.total - small.total >= 2 * 16384 * (28672 - 256)
+
+
+def test_gemm_dispatch(L):
+    """Kernel choice by shape (host only), including the degenerate shapes:
+    the large backward kernel reads two weight steps before its loop, so an
+    empty contraction (N = 0) must never reach it."""
+    fp, bp = L.lib.int8_linear_forward_plan, L.lib.int8_linear_backward_plan
+    BF16, F16, F32 = L.I8L_BF16, L.I8L_F16, L.I8L_F32
+    # forward: (dtype, M, K, N)
+    assert fp(BF16, 4096, 4096, 4096) == 2          # 256 tiles of 256 x 256
+    assert fp(BF16, 4096, 4096, 11008) == 2
+    assert fp(F16, 2048, 4096, 4096) == 3           # 128 such tiles: half-width tiles
+    assert fp(F32, 600, 4, 16) == 1
+    assert fp(BF16, 4096, 4100, 4096) == 1          # K not a multiple of 16
+    assert fp(BF16, 0, 4096, 4096) == 0 and fp(BF16, 4096, 4096, 0) == 0
+    assert fp(BF16, 4096, 0, 4096) == 2             # K = 0: buffer loads past the end read zero
+    assert fp(7, 1, 1, 1) == L.I8L_EDTYPE and fp(BF16, -1, 1, 1) == L.I8L_EINVAL
+    assert fp(BF16, 8, L.I8L_MAX_K + 1, 8) == L.I8L_ESHAPE
+    # backward: (dtype, M, N, K)
+    assert bp(BF16, 4096, 4096, 4096) == 2
+    assert bp(BF16, 4096, 11008, 4096) == 2
+    assert bp(F16, 2048, 4096, 4096) == 3
+    assert bp(F32, 4096, 4096, 4096) == 1           # fp32 gradients: generic kernel
+    assert bp(BF16, 4096, 4100, 4096) == 1          # N % 8 != 0
+    assert bp(BF16, 2048, 0, 2048) == 1             # empty contraction: the generic kernel writes zeros
+    assert bp(F16, 2048, 0, 2048) == 1
+    assert bp(BF16, 0, 4096, 4096) == 0 and bp(BF16, 4096, 4096, 0) == 0
+    assert bp(BF16, 16384, 28672, 8192) == 2 and bp(BF16, 16384, 8192, 28672) == 2
+    assert bp(BF16, 4096, 1 << 20, 4096) == 1       # beyond the 32-bit buffer offsets
 
 
 def test_binding_rejects_mis_sized_results(L):

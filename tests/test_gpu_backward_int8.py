@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from tests._gpu import assert_bits_equal, assert_float_gate, dev, host
+from tests._gpu import assert_bits_equal, assert_float_gate, dev, host, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -176,6 +176,5 @@ def test_backward_int8_full_size_block(I8):
     CBt, SCBt, cbt, scbt = _weights_t(I8, W)
     del W
     G = workloads.make_grad(wl, li)
-    g = np.random.default_rng(0)
-    rows = np.array(sorted(set(g.choice(L.M, 24, replace=False).tolist()) | {0, L.M - 1}))
+    rows = tile_rows(L.M)
     _run_and_check(I8, G, dt, CBt, SCBt, cbt, scbt, rows=rows)

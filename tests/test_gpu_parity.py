@@ -141,7 +141,8 @@ def _forward_and_check(I8, A, dt, CB, SCB, cb, scb, bias, tau, cap=None, rows=No
     cnt = int(wsh[L.count:L.count + 4].view(np.int32)[0])
     assert cnt == q["outliers"].size
     k = min(cnt, capn)
-    assert_bits_equal(wsh[L.idx:L.idx + 4 * k].view(np.int32), q["outliers"][:k], "forward outlier list")
+    # the list holds every outlier column; the first cap of them are staged
+    assert_bits_equal(wsh[L.idx:L.idx + 4 * cnt].view(np.int32), q["outliers"], "forward outlier list")
     assert_bits_equal(wsh[L.scale:L.scale + 4 * M].view(np.float32), q["scale"], "SCA")
     assert_bits_equal(wsh[L.codes:L.codes + M * K].view(np.int8).reshape(M, K), q["codes"], "CA")
     if capn:
@@ -260,19 +261,47 @@ def test_backward_integer_case_exact(I8):
     assert np.array_equal(host(gA), ref.astype(np.float32))
 
 
+# more outlier columns than the staging width: the epilogue reads the values
+# of the columns past `cap` from the input itself. Shapes for the generic
+# kernel and for both large-tile kernels (256 x 128 and 256 x 256 tiles);
+# 21 seeded columns, so that the outlier product runs past the 16 columns the
+# large kernels stage in LDS
+OSHAPES = [(300, 1040, 520), (1024, 1024, 4096), (1040, 512, 8320)]
+
+
 @pytest.mark.parametrize("dt", DTS)
-def test_forward_outlier_overflow_reported(I8, dt):
-    M, K, N = 40, 64, 32
-    A, W, b, _ = _layer(dt, M, K, N, 4, n_out=6)
-    CB, SCB = _gpu_weights(I8, W)
-    ws = I8.forward_workspace(M, K, 2, "cuda:0")
-    I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt), 6.0, cap=2, workspace=ws)
-    with pytest.raises(I8.Int8LinError) as e:
-        I8.forward_check(ws, M, K, 2)
-    assert e.value.code == -6
-    ws2 = I8.forward_workspace(M, K, K, "cuda:0")
-    I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt), 6.0, cap=K, workspace=ws2)
-    assert I8.forward_check(ws2, M, K, K) >= 6
+@pytest.mark.parametrize("M,K,N", OSHAPES)
+def test_forward_outliers_beyond_staging(I8, dt, M, K, N):
+    A, W, b, _ = _layer(dt, M, K, N, 4, n_out=21)
+    CB, SCB, cb, scb = _check_weights(I8, W)
+    outs = {}
+    for cap in (K, 0, 2, 16, 17):
+        print(f"  [{dt} {M}x{K}x{N}] cap={cap}", flush=True)
+        out, f = _forward_and_check(I8, A, dt, CB, SCB, cb, scb, b, 6.0, cap=cap)
+        assert f["q"]["outliers"].size >= 21
+        outs[cap] = host(out)
+    for cap in (0, 2, 16, 17):       # identical bits whatever the staging width
+        assert_bits_equal(outs[cap], outs[K], f"out with cap={cap} against cap=K")
+    ws = I8.forward_workspace(M, K, 3, "cuda:0")
+    I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt), 6.0, cap=3, workspace=ws)
+    assert I8.forward_check(ws, M, K, 3) == f["q"]["outliers"].size
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_backward_empty_contraction_is_zero(I8, dt):
+    """N = 0 output features with M = K = 2048 (a shape whose non-empty
+    version takes the large-tile kernel): grad_A is all zeros and grad_bias
+    empty; the empty weight arrives as a NULL pointer."""
+    M, K = 2048, 2048
+    assert I8.lib.int8_linear_backward_plan(I8.DTYPE_CODE[TORCH[dt]], M, 0, K) == 1
+    G = torch.empty((M, 0), dtype=TORCH[dt], device="cuda:0")
+    CB = torch.empty((0, K), dtype=torch.int8, device="cuda:0")
+    SCB = torch.empty((0,), dtype=torch.float32, device="cuda:0")
+    gA = torch.full((M, K), 7.0, dtype=TORCH[dt], device="cuda:0")
+    gA, gb = I8.int8_linear_backward_input(G, CB, SCB, with_grad_bias=True, grad_A=gA)
+    torch.cuda.synchronize()
+    assert gb.numel() == 0
+    assert torch.count_nonzero(gA).item() == 0
 
 
 def test_empty_and_degenerate(I8):

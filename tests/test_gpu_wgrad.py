@@ -17,7 +17,7 @@ import torch
 import oracle
 import workloads
 from oracle.formats import to_f64, to_half, ulp
-from tests._gpu import assert_bits_equal, dev, host
+from tests._gpu import assert_bits_equal, dev, host, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -129,8 +129,7 @@ def test_wgrad_full_size_block(I8):
     G = workloads.make_grad(wl, li)
     gW = I8.int8_linear_backward_weight(dev(G, wl.dtype), dev(A, wl.dtype))
     torch.cuda.synchronize()
-    g = np.random.default_rng(0)
-    rows = np.array(sorted(set(g.choice(L.N, 24, replace=False).tolist()) | {0, L.N - 1}))
+    rows = tile_rows(L.N)          # one weight row in every 256-row output tile
     r = oracle.linear_backward_weight(G, A, wl.dtype, rows=rows)
     assert_accum_gate(host(gW.index_select(0, torch.from_numpy(rows).to("cuda:0"))), wl.dtype, r["y"], G, A,
                       rows, "grad_W (sampled rows)")

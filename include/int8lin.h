@@ -60,9 +60,11 @@ enum {
   I8L_ESHAPE = -3,     /* size beyond what the kernels index, or K > I8L_MAX_K */
   I8L_EWORKSPACE = -4, /* workspace NULL or smaller than required */
   I8L_EHIP = -5,       /* a HIP launch or copy failed */
-  I8L_EOVERFLOW = -6   /* reserved: no call returns it (the forward handles any number of
+  I8L_EOVERFLOW = -6,  /* reserved: no call returns it (the forward handles any number of
                           outlier columns; int8_quantize_rowwise reports |O| > cap
                           through its count) */
+  I8L_ESCRATCH = -7    /* problem larger than the static scratch of the allocation-free
+                          forward */
 };
 
 /* Largest contraction length whose int32 accumulator cannot overflow:
@@ -137,6 +139,34 @@ int int8_linear_forward_workspace_layout(int64_t M, int64_t K, int32_t cap, i8l_
 int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
                         int64_t N, const void* bias, float threshold, int32_t cap, void* out, int32_t* c32_debug,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): int8_linear_forward with the same inputs, outputs, arithmetic
+ * and errors, but its workspace is a static array inside the library
+ * (I8L_NOALLOC_SCRATCH_BYTES = 64 MiB per GPU, reserved on each GPU the
+ * library runs on until the process ends) and the outlier staging width is
+ * min(K, 64) (further outlier columns are read from A, as in the forward).
+ * The call allocates nothing and calls no allocating routine.
+ *   int8_linear_forward_noalloc_bytes(M, K): scratch bytes a call of M x K
+ *     needs (the forward workspace at that staging width);
+ *   int8_linear_forward_noalloc_max_bytes(): the limit, I8L_NOALLOC_SCRATCH_BYTES.
+ * A problem needing more (for instance M * K above about 63 million) is
+ * rejected with I8L_ESCRATCH on the host, before any HIP call. The first call
+ * on a GPU looks up that GPU's copy of the array (the current device must be
+ * the stream's). Every call on one GPU shares that copy: calls that overlap
+ * on one GPU (different streams, or different host threads without
+ * ordering) race and give wrong results; calls in one stream are ordered and
+ * safe. Nothing in the array needs to start at zero.
+ * ------------------------------------------------------------------------ */
+#define I8L_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+size_t int8_linear_forward_noalloc_bytes(int64_t M, int64_t K);
+size_t int8_linear_forward_noalloc_max_bytes(void);
+
+int int8_linear_forward_noalloc(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
+                                int64_t N, const void* bias, float threshold, void* out, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * Outlier flags handed over by the producer of the input (EasyDeL discussion

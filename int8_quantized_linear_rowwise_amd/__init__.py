@@ -27,7 +27,7 @@ __all__ = [
     "int8_linear_backward_weight", "Int8LinearTrainableFunction", "Int8LinearTrainable",
     "outlier_flags_buffer", "silu_outlier_flags", "int8_linear_forward_flagged",
     "Int8LinearFunction", "Int8Linear", "Int8LinError", "forward_workspace", "forward_layout",
-    "forward_check", "default_cap", "DTYPE_CODE", "I8L_MAX_K",
+    "forward_check", "default_cap", "int8_linear_forward_noalloc", "DTYPE_CODE", "I8L_MAX_K",
 ]
 
 DTYPE_CODE = {torch.float32: I8L_F32, torch.float16: I8L_F16, torch.bfloat16: I8L_BF16}
@@ -172,6 +172,30 @@ def int8_linear_forward(A: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor, bi
                                   _dev(bias, "bias"), float(threshold), cap, _dev(out, "out"), _dev(c32, "c32"),
                                   workspace.data_ptr(), workspace.numel(), _stream(A.device)),
           "int8_linear_forward")
+    return out
+
+
+def int8_linear_forward_noalloc(A: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,
+                                bias: Optional[torch.Tensor] = None, threshold: float = 6.0,
+                                out: Optional[torch.Tensor] = None):
+    """int8_linear_forward on the library's static per-GPU scratch: the C call
+    allocates nothing (pass `out` to allocate nothing here either). Calls that
+    overlap on one GPU share the scratch and race; sizes beyond the scratch
+    raise Int8LinError (I8L_ESCRATCH)."""
+    if A.dim() != 2 or CB.dim() != 2:
+        raise ValueError("A and CB must be 2-D")
+    M, K = A.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or SCB.shape != (N,) or CB.dtype != torch.int8 or SCB.dtype != torch.float32:
+        raise ValueError("CB must be N x K int8 and SCB N fp32")
+    if bias is not None and (bias.shape != (N,) or bias.dtype != A.dtype):
+        raise ValueError("bias must have shape (N,) and A's dtype")
+    _check_out(out, (M, N), A.dtype, "out")
+    if out is None:
+        out = _empty((M, N), A.dtype, A.device)
+    check(lib.int8_linear_forward_noalloc(_dev(A, "A"), _code(A), M, K, _dev(CB, "CB"), _dev(SCB, "SCB"), N,
+                                          _dev(bias, "bias"), float(threshold), _dev(out, "out"), _stream(A.device)),
+          "int8_linear_forward_noalloc")
     return out
 
 

@@ -13,6 +13,8 @@ LIB_PATH = os.environ.get("I8L_LIBRARY", os.path.join(_HERE, "libint8lin.so"))
 
 I8L_F32, I8L_F16, I8L_BF16 = 0, 1, 2
 I8L_OK, I8L_EINVAL, I8L_EDTYPE, I8L_ESHAPE, I8L_EWORKSPACE, I8L_EHIP, I8L_EOVERFLOW = 0, -1, -2, -3, -4, -5, -6
+I8L_ESCRATCH = -7
+I8L_NOALLOC_SCRATCH_BYTES = 64 << 20
 I8L_MAX_K = 133144
 I8L_MAX_COLS = 262144
 
@@ -35,6 +37,9 @@ SIGNATURES = {
                                    _vp]),
     "int8_linear_forward_check": (_int, [_vp, _i64, _i64, _i32, _vp, ctypes.POINTER(_i32)]),
     "int8_linear_forward_plan": (_int, [_int, _i64, _i64, _i64]),
+    "int8_linear_forward_noalloc_bytes": (_sz, [_i64, _i64]),
+    "int8_linear_forward_noalloc_max_bytes": (_sz, []),
+    "int8_linear_forward_noalloc": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _f32, _vp, _vp]),
     "int8_linear_backward_plan": (_int, [_int, _i64, _i64, _i64]),
     "int8_linear_backward_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "int8_linear_backward_input": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),

@@ -4,8 +4,16 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/int8lin.h"
 #include "kernels.hpp"
+
+// Scratch of int8_linear_forward_noalloc: one copy on every GPU the library
+// runs on, held until the process ends. Host code never uses this name as an
+// address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[I8L_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -40,6 +48,33 @@ bool fwd_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* L) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? I8L_OK : I8L_EHIP; }
 
+// outlier staging width of the allocation-free forward (further outlier
+// columns are read from A by the epilogue)
+constexpr int32_t NOALLOC_CAP = 64;
+constexpr int MAX_DEVICES = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+// Device address of the current GPU's copy of `scratch`, looked up once per
+// device with that device current and kept for later calls.
+hipError_t noalloc_scratch(void** p) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (q == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = q;
+  }
+  *p = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -53,6 +88,8 @@ const char* int8_linear_strerror(int code) {
     case I8L_EWORKSPACE: return "workspace missing or too small";
     case I8L_EHIP: return "HIP launch or copy failed";
     case I8L_EOVERFLOW: return "more outlier columns than the outlier buffer capacity";
+    case I8L_ESCRATCH:
+      return "problem too large for the library's static scratch (see int8_linear_forward_noalloc_max_bytes)";
     default: return "unknown error";
   }
 }
@@ -129,6 +166,39 @@ int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const in
                         int64_t N, const void* bias, float threshold, int32_t cap, void* out, int32_t* c32,
                         void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(A, dtype, M, K, CB, SCB, N, bias, threshold, nullptr, cap, out, c32, ws, ws_bytes, stream);
+}
+
+size_t int8_linear_forward_noalloc_max_bytes(void) { return I8L_NOALLOC_SCRATCH_BYTES; }
+
+size_t int8_linear_forward_noalloc_bytes(int64_t M, int64_t K) {
+  i8l_forward_layout L;
+  if (M < 0 || K < 0 || !fwd_layout(M, K, K < NOALLOC_CAP ? (int32_t)K : NOALLOC_CAP, &L)) return 0;
+  return L.total;
+}
+
+int int8_linear_forward_noalloc(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
+                                int64_t N, const void* bias, float threshold, void* out, void* stream) {
+  // argument errors first, on the host, as in int8_linear_forward
+  if (!valid_dtype(dtype)) return I8L_EDTYPE;
+  if (M < 0 || K < 0 || N < 0) return I8L_EINVAL;
+  if (M > INT32_MAX || N > INT32_MAX || K > I8L_MAX_K || M * K > ((int64_t)1 << 40) ||
+      M * N > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40))
+    return I8L_ESHAPE;
+  if (M > 0 && N > 0) {
+    if (out == nullptr || SCB == nullptr) return I8L_EINVAL;
+    if (K > 0 && (A == nullptr || CB == nullptr)) return I8L_EINVAL;
+  }
+  const int32_t cap = K < NOALLOC_CAP ? (int32_t)K : NOALLOC_CAP;
+  i8l_forward_layout L;
+  fwd_layout(M, K, cap, &L);
+  if (L.total > I8L_NOALLOC_SCRATCH_BYTES) return I8L_ESCRATCH;
+  if (M == 0 || N == 0) return I8L_OK;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return I8L_EHIP;
+  // no buffer of the call needs to start at zero: the quantizer writes its
+  // flag words, list, count, codes and scales before the GEMM reads them
+  return forward_impl(A, dtype, M, K, CB, SCB, N, bias, threshold, nullptr, cap, out, nullptr, ws,
+                      I8L_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t int8_outlier_flags_words(int64_t rows, int64_t cols) {

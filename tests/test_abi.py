@@ -54,7 +54,7 @@ def test_exports_are_plain_c(L):
 
 
 def test_strerror(L):
-    for c in (0, -1, -2, -3, -4, -5, -6, -99):
+    for c in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert isinstance(L.lib.int8_linear_strerror(c), bytes)
     assert L.lib.int8_linear_strerror(-4).startswith(b"workspace")
 
@@ -301,3 +301,32 @@ def test_binding_rejects_mis_sized_results(L):
     for f in bad:
         with pytest.raises(ValueError):
             f()
+
+
+def test_noalloc_forward_host_errors(L):
+    """The allocation-free forward validates like the forward and rejects a
+    problem beyond its static scratch on the host, before any HIP call."""
+    f = L.lib.int8_linear_forward_noalloc
+    cap_max = L.lib.int8_linear_forward_noalloc_max_bytes()
+    assert cap_max == L.I8L_NOALLOC_SCRATCH_BYTES == 64 << 20
+    need = L.lib.int8_linear_forward_noalloc_bytes
+    assert need(4096, 11008) <= cap_max               # the 7B block's widest input fits
+    assert need(16384, 28672) > cap_max               # the 70B down layer does not
+    assert need(300, 1040) == L.lib.int8_linear_forward_workspace_bytes(300, 1040, 64)
+    assert need(5, 16) == L.lib.int8_linear_forward_workspace_bytes(5, 16, 16)
+    assert need(-1, 4) == 0
+    base = dict(A=FAKE, dt=2, M=8, K=64, CB=FAKE, SCB=FAKE, N=32, b=None, tau=6.0, out=FAKE, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["A"], a["dt"], a["M"], a["K"], a["CB"], a["SCB"], a["N"], a["b"], a["tau"], a["out"], a["st"])
+
+    assert call(dt=9) == L.I8L_EDTYPE
+    assert call(M=-1) == L.I8L_EINVAL
+    assert call(A=0) == L.I8L_EINVAL
+    assert call(out=0) == L.I8L_EINVAL
+    assert call(K=L.I8L_MAX_K + 1) == L.I8L_ESHAPE
+    assert call(M=16384, K=28672, N=8192) == L.I8L_ESCRATCH
+    assert call(M=8192, K=8192) == L.I8L_ESCRATCH     # 64 MiB of codes alone
+    assert call(M=0) == L.I8L_OK and call(N=0) == L.I8L_OK
+    assert b"static scratch" in L.lib.int8_linear_strerror(L.I8L_ESCRATCH)

@@ -381,6 +381,80 @@ def cpu_baseline(wl, target_s, threshold):
                       f"forward + backward, numpy float64, {tt:.1f} s"}
 
 
+def run_peaks():
+    """Roofline constants measured on this GPU: MFMA-only loops (the two
+    instructions of the layer's GEMMs, one and two waves per SIMD) with the
+    shader clock they ran at, and HBM read / copy bandwidth of large buffers."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "int8_quantized_linear_rowwise_amd", "libi8lpeaks.so"))
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+    lib.i8l_peak_mfma.argtypes = [i32, i32, i32, vp, vp, vp]
+    lib.i8l_peak_mfma_macs.restype = i64
+    lib.i8l_peak_mfma_macs.argtypes = [i32]
+    lib.i8l_peak_read.argtypes = [vp, i64, vp, i32, vp]
+    lib.i8l_peak_copy.argtypes = [vp, vp, i64, i32, vp]
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    out = {"mfma": [], "hbm": []}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for kind, name, peak in ((0, "v_mfma_i32_32x32x32_i8", PEAK_INT8_TOPS), (1, "v_mfma_f32_32x32x16_f16", PEAK_F16_TFLOPS)):
+        for wps in (1, 2):
+            blocks, iters = cus * wps, 40000
+            sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+            clk = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+
+            def go():
+                rc = lib.i8l_peak_mfma(kind, blocks, iters, sink.data_ptr(), clk.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"i8l_peak_mfma: hip error {rc}")
+
+            t = timed(go, 3)
+            c = clk.view(-1, 4).cpu().double()
+            ghz = ((c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 100e6) / 1e9).median().item()
+            ops = blocks * 4 * iters * 8 * 2 * lib.i8l_peak_mfma_macs(kind)
+            rate = ops / t / 1e12
+            out["mfma"].append({"instruction": name, "waves_per_simd": wps, "tops": round(rate, 1),
+                                "pct_published": round(100 * rate / peak, 1), "published": peak,
+                                "shader_clock_ghz": round(ghz, 3),
+                                "pct_of_published_at_that_clock": round(100 * rate / (peak * ghz / 2.4), 1)})
+            log(f"[peaks] {name} {wps} wave/SIMD: {rate:.0f} T/s at {ghz:.2f} GHz")
+    nbytes = 4 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    blocks = cus * 8
+    t = timed(lambda: lib.i8l_peak_read(src.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream), 5)
+    out["hbm"].append({"kernel": "read 4 GiB", "gbs": round(nbytes / t / 1e9, 1),
+                       "pct_published": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1)})
+    t = timed(lambda: lib.i8l_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, blocks, stream.cuda_stream), 5)
+    out["hbm"].append({"kernel": "copy 4 GiB (read + write)", "gbs": round(2 * nbytes / t / 1e9, 1),
+                       "pct_published": round(100 * 2 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1)})
+    t = timed(lambda: dst.copy_(src), 5)
+    out["hbm"].append({"kernel": "torch copy_ 4 GiB (read + write)", "gbs": round(2 * nbytes / t / 1e9, 1),
+                       "pct_published": round(100 * 2 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1)})
+    out["compute_units"] = cus
+    out["device"] = torch.cuda.get_device_name(0)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,6 +464,8 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the roofline constants (MFMA-only loops, HBM read/copy) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -397,6 +473,10 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.peaks:
+        print(json.dumps({"peaks": run_peaks()}), flush=True)
+        return
 
     import workloads
     wl = workloads.WORKLOADS[args.workload]

@@ -1,4 +1,5 @@
-"""Build the HIP library libint8lin.so in-tree for gfx950 (hipcc, no GPU needed).
+"""Build the HIP library libint8lin.so in-tree for gfx950 (hipcc, no GPU needed),
+and libi8lpeaks.so, the measurement kernels of the benchmark's --peaks mode.
 
     python int8_quantized_linear_rowwise_amd/build.py [--jobs N]
 
@@ -19,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libint8lin.so")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "quantize.hip", "gemm_fwd.hip", "gemm_bwd.hip", "gemm_wgrad.hip"]
+PEAKS_SRC = "peaks.hip"
+PEAKS_OUT = os.path.join(PKG, "libi8lpeaks.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("I8L_OFFLOAD_ARCH", "gfx950")
@@ -44,15 +47,16 @@ def _compile(src: str) -> str:
 def build(jobs: int = 4, verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
-    if verbose:
-        print(f"built {OUT}")
+        objs = list(ex.map(_compile, SOURCES + [PEAKS_SRC]))
+    for out, parts in ((OUT, objs[:-1]), (PEAKS_OUT, objs[-1:])):
+        tmp = out + ".tmp"
+        cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *parts, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, out)
+        if verbose:
+            print(f"built {out}")
     return OUT
 
 

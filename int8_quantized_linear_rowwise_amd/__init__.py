@@ -68,12 +68,15 @@ def _empty(shape, dtype, device):
 # quantizer
 
 
-def int8_quantize_rowwise(X: torch.Tensor, threshold: float = 6.0, cap: Optional[int] = None):
+def int8_quantize_rowwise(X: torch.Tensor, threshold: float = 6.0, cap: Optional[int] = None,
+                          workspace: Optional[torch.Tensor] = None):
     """Row-wise int8 quantization of a 2-D tensor with outlier-column split.
 
     Returns (codes int8 R x C, row_scale fp32 R, outlier_idx int32 cap,
     outlier_count int32 (1,), sub fp16 R x cap). Only the first
-    min(count, cap) outlier entries / sub columns are meaningful."""
+    min(count, cap) outlier entries / sub columns are meaningful.
+    workspace: optional uint8 buffer of at least
+    int8_quantize_rowwise_workspace_bytes(R, C) bytes, reused across calls."""
     if X.dim() != 2:
         raise ValueError("X must be 2-D (flatten leading dimensions)")
     R, C = X.shape
@@ -85,7 +88,12 @@ def int8_quantize_rowwise(X: torch.Tensor, threshold: float = 6.0, cap: Optional
     count = _empty((1,), torch.int32, dev)
     sub = _empty((R, max(cap, 1)), torch.float16, dev)
     wsb = lib.int8_quantize_rowwise_workspace_bytes(R, C)
-    ws = _empty((max(wsb, 1),), torch.uint8, dev)
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or workspace.numel() < wsb:
+            raise ValueError(f"workspace must be uint8 with at least {wsb} bytes")
+        ws, wsb = workspace, workspace.numel()
+    else:
+        ws = _empty((max(wsb, 1),), torch.uint8, dev)
     check(lib.int8_quantize_rowwise(_dev(X, "X"), _code(X), R, C, float(threshold), _dev(codes, "codes"),
                                     _dev(scale, "scale"), idx.data_ptr(), count.data_ptr(), sub.data_ptr(), cap,
                                     ws.data_ptr(), wsb, _stream(dev)),

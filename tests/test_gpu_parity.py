@@ -36,18 +36,24 @@ def _quant_case(dt, R, C, seed, n_out=3, scale=20.0):
 
 
 def _check_quant(I8, X, dt, tau, cap=None):
+    """Two calls on one workspace that starts as arbitrary bytes (workspaces
+    need no initialisation and are reused across calls)."""
     R, C = X.shape
-    codes, scale, idx, cnt, sub = I8.int8_quantize_rowwise(dev(X, dt), tau, cap)
-    torch.cuda.synchronize()
     q = oracle.quantize_rowwise(X, dt, tau)
-    n = int(host(cnt)[0])
-    assert n == q["outliers"].size, (n, q["outliers"].size)
     capn = C if cap is None else cap
-    k = min(n, capn)
-    assert_bits_equal(host(codes), q["codes"], "codes")
-    assert_bits_equal(host(scale), q["scale"], "row scale")
-    assert_bits_equal(host(idx)[:k], q["outliers"][:k], "outlier index list")
-    assert_bits_equal(host(sub)[:, :k], q["sub"][:, :k], "outlier sub-matrix")
+    wsb = I8.lib.int8_quantize_rowwise_workspace_bytes(R, C)
+    ws = torch.full((max(wsb, 1),), 0xA7, dtype=torch.uint8, device="cuda:0")
+    Xd = dev(X, dt)
+    for call in range(2):
+        codes, scale, idx, cnt, sub = I8.int8_quantize_rowwise(Xd, tau, cap, workspace=ws)
+        torch.cuda.synchronize()
+        n = int(host(cnt)[0])
+        assert n == q["outliers"].size, (call, n, q["outliers"].size)
+        k = min(n, capn)
+        assert_bits_equal(host(codes), q["codes"], f"codes (call {call})")
+        assert_bits_equal(host(scale), q["scale"], f"row scale (call {call})")
+        assert_bits_equal(host(idx)[:k], q["outliers"][:k], f"outlier index list (call {call})")
+        assert_bits_equal(host(sub)[:, :k], q["sub"][:, :k], f"outlier sub-matrix (call {call})")
     return q
 
 
@@ -129,10 +135,13 @@ def _forward_and_check(I8, A, dt, CB, SCB, cb, scb, bias, tau, cap=None, rows=No
     N = cb.shape[0]
     capn = K if cap is None else cap
     ws = I8.forward_workspace(M, K, capn, "cuda:0")
+    ws.fill_(0x5C)                   # arbitrary bytes: workspaces need no initialisation
     c32 = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
-    out = I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(bias, dt) if bias is not None else None, tau, capn,
-                                 c32=c32, workspace=ws)
+    Ad, bd = dev(A, dt), (dev(bias, dt) if bias is not None else None)
+    out0 = I8.int8_linear_forward(Ad, CB, SCB, bd, tau, capn, workspace=ws)
+    out = I8.int8_linear_forward(Ad, CB, SCB, bd, tau, capn, c32=c32, workspace=ws)
     torch.cuda.synchronize()
+    assert_bits_equal(host(out0), host(out), "out of two calls on one workspace")
     f = oracle.linear_forward(A, dt, cb, scb, bias, tau, rows=rows)
     q = f["q"]
     # the forward's own quantization, read back from its workspace

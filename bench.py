@@ -74,7 +74,7 @@ def make_gpu_inputs(wl, n_sets, seed_base=1234):
                            gA=torch.empty((L.M, L.K), dtype=dt, device=dev),
                            gb=torch.empty((L.N,), dtype=dt, device=dev) if L.has_bias else None,
                            cap=I8.default_cap(L.K),
-                           wsf=I8.forward_workspace(L.M, L.K, I8.default_cap(L.K), dev),
+                           wsf=I8.forward_workspace(L.M, L.K, L.N, I8.default_cap(L.K), dev),
                            wsb=torch.empty((max(1, I8.lib.int8_linear_backward_workspace_bytes(
                                L.M, L.N, int(L.has_bias))),), dtype=torch.uint8, device=dev)))
     torch.cuda.synchronize()
@@ -106,7 +106,7 @@ def run_gpu(wl, steps, warmup, n_sets, threshold):
     torch.cuda.synchronize()
     # outlier columns found by the forward (any number is handled; the first
     # `cap` are staged, later ones read from the input by the epilogue)
-    n_outliers = [I8.forward_check(ly["wsf"], ly["L"].M, ly["L"].K, ly["cap"]) for ly in layers]
+    n_outliers = [I8.forward_check(ly["wsf"], ly["L"].M, ly["L"].K, ly["L"].N, ly["cap"]) for ly in layers]
 
     # one step = forward of every layer (in order), then backward of every layer
     # (reverse order), as in a training step; one event pair brackets each phase

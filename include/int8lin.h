@@ -116,10 +116,16 @@ int int8_quantize_rowwise(const void* X, int dtype, int64_t rows, int64_t cols, 
  * values of the first cap outlier columns are staged there by the quantizer;
  * the epilogue reads those of any further outlier column from A itself (the
  * same fp16 cast), so every |O| <= K is handled and the output is complete
- * for any cap. A small cap (a few times the expected |O|) keeps the
- * workspace at about M*K + 2*M*cap bytes.
+ * for any cap. The row pass also writes the dequantized weight values of
+ * the first wcap outlier columns, wcap = cap rounded up to a multiple of 8
+ * and at most 256 (N x wcap fp16: the weight side of the outlier product,
+ * rebuilt from CB on every call), so that the epilogue reads both operands
+ * of that product as contiguous rows; the weight values of further columns
+ * are rebuilt from CB by the epilogue. A small cap (a few times the expected
+ * |O|) keeps the workspace at about M*K + 2*(M + N)*cap bytes.
  * The workspace holds the quantized activation (CA, SCA), the full outlier
- * list (K entries), subA and the quantizer's flag words; its layout is
+ * list (K entries), subA, the weight slice and the quantizer's flag words;
+ * its layout is
  * reported by int8_linear_forward_workspace_layout so that tests can read it
  * back. A must stay unchanged until the call has run (it is read twice by the
  * quantizer and again by the epilogue).
@@ -130,11 +136,12 @@ typedef struct {
   size_t scale;   /* fp32[M] SCA */
   size_t codes;   /* int8[M*K] CA */
   size_t sub;     /* fp16[M*cap] subA: A16[:, O[j]] for j < min(|O|, cap) */
+  size_t wsub;    /* fp16[N*wcap] (wcap above): Wdq[n, O[j]] for j < min(|O|, wcap) */
   size_t total;   /* bytes required */
 } i8l_forward_layout;
 
-size_t int8_linear_forward_workspace_bytes(int64_t M, int64_t K, int32_t cap);
-int int8_linear_forward_workspace_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* layout);
+size_t int8_linear_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t cap);
+int int8_linear_forward_workspace_layout(int64_t M, int64_t K, int64_t N, int32_t cap, i8l_forward_layout* layout);
 
 int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
                         int64_t N, const void* bias, float threshold, int32_t cap, void* out, int32_t* c32_debug,
@@ -149,10 +156,10 @@ int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const in
  * library runs on until the process ends) and the outlier staging width is
  * min(K, 64) (further outlier columns are read from A, as in the forward).
  * The call allocates nothing and calls no allocating routine.
- *   int8_linear_forward_noalloc_bytes(M, K): scratch bytes a call of M x K
- *     needs (the forward workspace at that staging width);
+ *   int8_linear_forward_noalloc_bytes(M, K, N): scratch bytes a call needs
+ *     (the forward workspace at that staging width);
  *   int8_linear_forward_noalloc_max_bytes(): the limit, I8L_NOALLOC_SCRATCH_BYTES.
- * A problem needing more (for instance M * K above about 63 million) is
+ * A problem needing more (about M*K + 128*(M + N) bytes above 64 MiB) is
  * rejected with I8L_ESCRATCH on the host, before any HIP call. The first call
  * on a GPU looks up that GPU's copy of the array (the current device must be
  * the stream's). Every call on one GPU shares that copy: calls that overlap
@@ -162,7 +169,7 @@ int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const in
  * ------------------------------------------------------------------------ */
 #define I8L_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
-size_t int8_linear_forward_noalloc_bytes(int64_t M, int64_t K);
+size_t int8_linear_forward_noalloc_bytes(int64_t M, int64_t K, int64_t N);
 size_t int8_linear_forward_noalloc_max_bytes(void);
 
 int int8_linear_forward_noalloc(const void* A, int dtype, int64_t M, int64_t K, const int8_t* CB, const float* SCB,
@@ -206,10 +213,10 @@ int int8_linear_forward_flagged(const void* A, int dtype, int64_t M, int64_t K, 
                                 size_t workspace_bytes, void* stream);
 
 /* Synchronises `stream` and reads the outlier count |O| of the last forward
- * that used `workspace` (laid out for M, K, cap) into *count (if non-NULL).
+ * that used `workspace` (laid out for M, K, N, cap) into *count (if non-NULL).
  * Returns I8L_OK, or I8L_EINVAL / I8L_EHIP. The forward's output is complete
  * for every count, so this call is a diagnostic, not a required check. */
-int int8_linear_forward_check(const void* workspace, int64_t M, int64_t K, int32_t cap, void* stream,
+int int8_linear_forward_check(const void* workspace, int64_t M, int64_t K, int64_t N, int32_t cap, void* stream,
                               int32_t* count);
 
 /* Which GEMM kernel a call of this shape launches, for operands with the

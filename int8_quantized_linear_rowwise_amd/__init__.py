@@ -117,14 +117,14 @@ def quantize_weight_colwise(W: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor
 # forward
 
 
-def forward_layout(M: int, K: int, cap: int) -> _lib.ForwardLayout:
+def forward_layout(M: int, K: int, N: int, cap: int) -> _lib.ForwardLayout:
     L = _lib.ForwardLayout()
-    check(lib.int8_linear_forward_workspace_layout(M, K, cap, L), "int8_linear_forward_workspace_layout")
+    check(lib.int8_linear_forward_workspace_layout(M, K, N, cap, L), "int8_linear_forward_workspace_layout")
     return L
 
 
-def forward_workspace(M: int, K: int, cap: int, device) -> torch.Tensor:
-    n = lib.int8_linear_forward_workspace_bytes(M, K, cap)
+def forward_workspace(M: int, K: int, N: int, cap: int, device) -> torch.Tensor:
+    n = lib.int8_linear_forward_workspace_bytes(M, K, N, cap)
     return _empty((max(n, 1),), torch.uint8, device)
 
 
@@ -132,17 +132,18 @@ DEFAULT_CAP = 256
 
 
 def default_cap(K: int) -> int:
-    """Columns of the forward workspace's fp16 outlier sub-matrix: the values
-    of further outlier columns are read from the input by the GEMM epilogue,
-    so this only sizes the staging buffer (the output is complete for any
-    number of outlier columns)."""
+    """Columns of the forward workspace's fp16 outlier sub-matrix (and, up to
+    256, of the weight's dequantized outlier slice): the values of further
+    outlier columns are read from the input and the int8 weights by the GEMM
+    epilogue, so this only sizes the staging buffers (the output is complete
+    for any number of outlier columns)."""
     return min(int(K), DEFAULT_CAP)
 
 
-def forward_check(ws: torch.Tensor, M: int, K: int, cap: int) -> int:
+def forward_check(ws: torch.Tensor, M: int, K: int, N: int, cap: int) -> int:
     """Synchronise and return the outlier count |O| of the last forward on ws."""
     c = ctypes_int32()
-    check(lib.int8_linear_forward_check(ws.data_ptr(), M, K, cap, _stream(ws.device), c),
+    check(lib.int8_linear_forward_check(ws.data_ptr(), M, K, N, cap, _stream(ws.device), c),
           "int8_linear_forward")
     return int(c.value)
 
@@ -175,7 +176,7 @@ def int8_linear_forward(A: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor, bi
     if out is None:
         out = _empty((M, N), A.dtype, A.device)
     if workspace is None:
-        workspace = forward_workspace(M, K, cap, A.device)
+        workspace = forward_workspace(M, K, N, cap, A.device)
     check(lib.int8_linear_forward(_dev(A, "A"), _code(A), M, K, _dev(CB, "CB"), _dev(SCB, "SCB"), N,
                                   _dev(bias, "bias"), float(threshold), cap, _dev(out, "out"), _dev(c32, "c32"),
                                   workspace.data_ptr(), workspace.numel(), _stream(A.device)),
@@ -255,7 +256,7 @@ def int8_linear_forward_flagged(A: torch.Tensor, flags: torch.Tensor, CB: torch.
     if out is None:
         out = _empty((M, N), A.dtype, A.device)
     if workspace is None:
-        workspace = forward_workspace(M, K, cap, A.device)
+        workspace = forward_workspace(M, K, N, cap, A.device)
     check(lib.int8_linear_forward_flagged(_dev(A, "A"), _code(A), M, K, _dev(flags, "flags"), flags.numel(),
                                           _dev(CB, "CB"),
                                           _dev(SCB, "SCB"), N, _dev(bias, "bias"), cap, _dev(out, "out"),

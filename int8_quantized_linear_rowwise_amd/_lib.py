@@ -24,20 +24,21 @@ _int = ctypes.c_int
 
 
 class ForwardLayout(ctypes.Structure):
-    _fields_ = [("count", _sz), ("idx", _sz), ("scale", _sz), ("codes", _sz), ("sub", _sz), ("total", _sz)]
+    _fields_ = [("count", _sz), ("idx", _sz), ("scale", _sz), ("codes", _sz), ("sub", _sz), ("wsub", _sz),
+                ("total", _sz)]
 
 
 SIGNATURES = {
     "int8_linear_strerror": (ctypes.c_char_p, [_int]),
     "int8_quantize_rowwise_workspace_bytes": (_sz, [_i64, _i64]),
     "int8_quantize_rowwise": (_int, [_vp, _int, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
-    "int8_linear_forward_workspace_bytes": (_sz, [_i64, _i64, _i32]),
-    "int8_linear_forward_workspace_layout": (_int, [_i64, _i64, _i32, ctypes.POINTER(ForwardLayout)]),
+    "int8_linear_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "int8_linear_forward_workspace_layout": (_int, [_i64, _i64, _i64, _i32, ctypes.POINTER(ForwardLayout)]),
     "int8_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _f32, _i32, _vp, _vp, _vp, _sz,
                                    _vp]),
-    "int8_linear_forward_check": (_int, [_vp, _i64, _i64, _i32, _vp, ctypes.POINTER(_i32)]),
+    "int8_linear_forward_check": (_int, [_vp, _i64, _i64, _i64, _i32, _vp, ctypes.POINTER(_i32)]),
     "int8_linear_forward_plan": (_int, [_int, _i64, _i64, _i64]),
-    "int8_linear_forward_noalloc_bytes": (_sz, [_i64, _i64]),
+    "int8_linear_forward_noalloc_bytes": (_sz, [_i64, _i64, _i64]),
     "int8_linear_forward_noalloc_max_bytes": (_sz, []),
     "int8_linear_forward_noalloc": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _f32, _vp, _vp]),
     "int8_linear_backward_plan": (_int, [_int, _i64, _i64, _i64]),

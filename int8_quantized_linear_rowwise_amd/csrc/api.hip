@@ -26,8 +26,8 @@ bool valid_dtype(int dt) { return dt == I8L_F32 || dt == I8L_F16 || dt == I8L_BF
 // quantizer scratch: the column flag words of each row slab ([slabs][ceil(cols / 32)])
 size_t quant_scratch_bytes(int64_t rows, int64_t cols) { return align_up(i8l::quant_scratch_words(rows, cols) * 4); }
 
-bool fwd_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* L) {
-  if (M < 0 || K < 0 || cap < 0) return false;
+bool fwd_layout(int64_t M, int64_t K, int64_t N, int32_t cap, i8l_forward_layout* L) {
+  if (M < 0 || K < 0 || N < 0 || cap < 0) return false;
   size_t off = 0;
   L->count = off;
   off += ALIGN;
@@ -40,6 +40,11 @@ bool fwd_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* L) {
   off += align_up((size_t)M * (size_t)K > 0 ? (size_t)M * (size_t)K : 1);
   L->sub = off;
   off += align_up((size_t)M * (size_t)cap * 2 > 0 ? (size_t)M * (size_t)cap * 2 : 2);
+  // the dequantized weight columns of the first wsub_width(cap) outlier columns
+  // (cap rounded up to a multiple of 8, at most 256)
+  const size_t wcap = (size_t)i8l::wsub_width(cap);
+  L->wsub = off;
+  off += align_up((size_t)N * wcap * 2 > 0 ? (size_t)N * wcap * 2 : 2);
   // quantizer scratch after the layout proper
   off += quant_scratch_bytes(M, K);
   L->total = off;
@@ -115,15 +120,15 @@ int int8_quantize_rowwise(const void* X, int dtype, int64_t rows, int64_t cols, 
                                          outlier_count, sub, cap, static_cast<uint32_t*>(ws), (hipStream_t)stream));
 }
 
-size_t int8_linear_forward_workspace_bytes(int64_t M, int64_t K, int32_t cap) {
+size_t int8_linear_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t cap) {
   i8l_forward_layout L;
-  if (!fwd_layout(M, K, cap, &L)) return 0;
+  if (!fwd_layout(M, K, N, cap, &L)) return 0;
   return L.total;
 }
 
-int int8_linear_forward_workspace_layout(int64_t M, int64_t K, int32_t cap, i8l_forward_layout* layout) {
+int int8_linear_forward_workspace_layout(int64_t M, int64_t K, int64_t N, int32_t cap, i8l_forward_layout* layout) {
   if (layout == nullptr) return I8L_EINVAL;
-  if (!fwd_layout(M, K, cap, layout)) return I8L_EINVAL;
+  if (!fwd_layout(M, K, N, cap, layout)) return I8L_EINVAL;
   return I8L_OK;
 }
 
@@ -140,7 +145,7 @@ static int forward_impl(const void* A, int dtype, int64_t M, int64_t K, const in
     if (K > 0 && (A == nullptr || CB == nullptr)) return I8L_EINVAL;
   }
   i8l_forward_layout L;
-  fwd_layout(M, K, cap, &L);
+  fwd_layout(M, K, N, cap, &L);
   if (ws == nullptr || ws_bytes < L.total) return I8L_EWORKSPACE;
   if ((uintptr_t)ws % ALIGN) return I8L_EINVAL;
   if (M == 0 || N == 0) return I8L_OK;
@@ -150,15 +155,20 @@ static int forward_impl(const void* A, int dtype, int64_t M, int64_t K, const in
   float* SCA = reinterpret_cast<float*>(w + L.scale);
   int8_t* CA = reinterpret_cast<int8_t*>(w + L.codes);
   uint16_t* subA = reinterpret_cast<uint16_t*>(w + L.sub);
+  uint16_t* wsub = reinterpret_cast<uint16_t*>(w + L.wsub);
+  const int wcap = i8l::wsub_width(cap);
   uint32_t* qscratch = reinterpret_cast<uint32_t*>(w + L.total - quant_scratch_bytes(M, K));
   hipStream_t st = (hipStream_t)stream;
   // the first cap outlier columns are staged in subA; the epilogue reads the
   // values of any further ones from A itself
+  // the row pass also writes wsub, the weight columns of the outlier columns
+  // dequantized (Wdq[n, O[j]], j < wcap), for the epilogue's outlier product
+  const i8l::OutlierWeights ow = {CB, SCB, (int)N, (int)K, wsub, wcap};
   hipError_t e = i8l::launch_quantize(dtype, A, M, (int)K, threshold, CA, SCA, idx, count, subA, cap, qscratch, st,
-                                      preflags, (int)K);
+                                      preflags, (int)K, &ow);
   if (e != hipSuccess) return I8L_EHIP;
-  e = i8l::launch_gemm_fwd(dtype, CA, SCA, (int)M, CB, SCB, (int)N, (int)K, subA, cap, A, idx, count, bias, out,
-                           c32, st);
+  e = i8l::launch_gemm_fwd(dtype, CA, SCA, (int)M, CB, SCB, (int)N, (int)K, subA, cap, wsub, wcap, A, idx, count,
+                           bias, out, c32, st);
   return hip_status(e);
 }
 
@@ -170,9 +180,9 @@ int int8_linear_forward(const void* A, int dtype, int64_t M, int64_t K, const in
 
 size_t int8_linear_forward_noalloc_max_bytes(void) { return I8L_NOALLOC_SCRATCH_BYTES; }
 
-size_t int8_linear_forward_noalloc_bytes(int64_t M, int64_t K) {
+size_t int8_linear_forward_noalloc_bytes(int64_t M, int64_t K, int64_t N) {
   i8l_forward_layout L;
-  if (M < 0 || K < 0 || !fwd_layout(M, K, K < NOALLOC_CAP ? (int32_t)K : NOALLOC_CAP, &L)) return 0;
+  if (M < 0 || K < 0 || N < 0 || !fwd_layout(M, K, N, K < NOALLOC_CAP ? (int32_t)K : NOALLOC_CAP, &L)) return 0;
   return L.total;
 }
 
@@ -190,7 +200,7 @@ int int8_linear_forward_noalloc(const void* A, int dtype, int64_t M, int64_t K, 
   }
   const int32_t cap = K < NOALLOC_CAP ? (int32_t)K : NOALLOC_CAP;
   i8l_forward_layout L;
-  fwd_layout(M, K, cap, &L);
+  fwd_layout(M, K, N, cap, &L);
   if (L.total > I8L_NOALLOC_SCRATCH_BYTES) return I8L_ESCRATCH;
   if (M == 0 || N == 0) return I8L_OK;
   void* ws = nullptr;
@@ -228,9 +238,10 @@ int int8_linear_forward_flagged(const void* A, int dtype, int64_t M, int64_t K, 
   return forward_impl(A, dtype, M, K, CB, SCB, N, bias, 0.0f, flags, cap, out, c32_debug, ws, ws_bytes, stream);
 }
 
-int int8_linear_forward_check(const void* ws, int64_t M, int64_t K, int32_t cap, void* stream, int32_t* count) {
+int int8_linear_forward_check(const void* ws, int64_t M, int64_t K, int64_t N, int32_t cap, void* stream,
+                              int32_t* count) {
   i8l_forward_layout L;
-  if (ws == nullptr || !fwd_layout(M, K, cap, &L)) return I8L_EINVAL;
+  if (ws == nullptr || !fwd_layout(M, K, N, cap, &L)) return I8L_EINVAL;
   int32_t c = 0;
   hipStream_t st = (hipStream_t)stream;
   if (hipMemcpyAsync(&c, static_cast<const char*>(ws) + L.count, sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
@@ -347,8 +358,8 @@ int int8_linear_backward_input_int8(const void* G, int dtype, int64_t M, int64_t
     // column-quantized weight copy: the forward kernel with K and N exchanged
     hipError_t e = i8l::launch_quantize(dtype, G, M, (int)N, 0.0f, CG, SG, nullptr, count, nullptr, 0, qscratch, st);
     if (e != hipSuccess) return I8L_EHIP;
-    e = i8l::launch_gemm_fwd(dtype, CG, SG, (int)M, CBt, SCBt, (int)K, (int)N, nullptr, 0, nullptr, nullptr, count,
-                             nullptr, grad_A, c32_debug, st);
+    e = i8l::launch_gemm_fwd(dtype, CG, SG, (int)M, CBt, SCBt, (int)K, (int)N, nullptr, 0, nullptr, 0, nullptr,
+                             nullptr, count, nullptr, grad_A, c32_debug, st);
     if (e != hipSuccess) return I8L_EHIP;
   }
   if (grad_bias != nullptr && N > 0) {

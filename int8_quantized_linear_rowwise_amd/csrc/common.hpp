@@ -27,6 +27,18 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   const v2f f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h));
 }
+// fp16 value (RNE) of x after x has been rounded to fp32. A product written
+// straight into an fp16 conversion is otherwise compiled to one
+// mixed-precision FMA (v_fma_mixlo_f16), even with contraction off, which
+// rounds the exact product to fp16 in one step; that differs from rounding it
+// to fp32 first whenever the fp32 product lies exactly halfway between two
+// fp16 values. The empty asm statement (no instruction) keeps x an fp32
+// register value.
+__device__ __forceinline__ _Float16 half_of_f32(float x) {
+  asm("" : "+v"(x));
+  return (_Float16)x;
+}
+
 // Two fp32 values -> two fp16 values packed in a word (RNE).
 __device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
   const v2f f = {a, b};

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void k_gemm_bwd(const typename Elem<DT>::T* __
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int b = (int)(int8_t)(wraw[u][e] >> (8 * c));
-          h[e] = (_Float16)((float)b * wsig[u][e]);
+          h[e] = half_of_f32((float)b * wsig[u][e]);
         }
         *reinterpret_cast<v8h*>(dW + (4 * kq + c) * LDN + 8 * ng) = h;
       }

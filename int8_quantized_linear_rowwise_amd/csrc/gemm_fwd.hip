@@ -56,11 +56,74 @@ __device__ __forceinline__ uint16_t outlier_half(const uint16_t* __restrict__ su
   return __builtin_bit_cast(uint16_t, to_half<DT>(A[(int64_t)m * K + idx[j]]));
 }
 
+// Outlier values j0 .. j0 + 7 of activation row m as one fp16 operand (zero
+// at and past cnt, or for a row outside the matrix): one 16-byte read of the
+// staged copy when the staging rows are 16-byte aligned and hold all eight.
+template <int DT>
+__device__ __forceinline__ v8h outlier_a8(const uint16_t* __restrict__ subA, int cap,
+                                          const typename Elem<DT>::T* __restrict__ A, int K,
+                                          const int32_t* __restrict__ idx, int m, bool mok, int j0, int cnt) {
+  v8h q;
+  if (mok && (cap & 7) == 0 && j0 + 8 <= cap) {
+    const v8h v = *reinterpret_cast<const v8h*>(subA + (int64_t)m * cap + j0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = (j0 + e < cnt) ? v[e] : (_Float16)0.0f;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      q[e] = (mok && j0 + e < cnt) ? __builtin_bit_cast(_Float16, outlier_half<DT>(subA, cap, A, K, idx, m, j0 + e))
+                                   : (_Float16)0.0f;
+  }
+  return q;
+}
+
+// Dequantized weight values Wdq[n, O[j]], j = j0 .. j0 + 7 (j0 % 8 == 0), as
+// one fp16 operand (zero at and past cnt, or for a row outside the matrix):
+// one 16-byte read of the slice the row quantizer wrote (wcap columns, a
+// multiple of 8), beyond it fp16(CB[n, O[j]] * (SCB[n] * (1/127))) rebuilt
+// from the int8 weights.
+__device__ __forceinline__ v8h outlier_w8(const uint16_t* __restrict__ wsub, int wcap,
+                                          const int8_t* __restrict__ CB, const float* __restrict__ SCB, int K,
+                                          const int32_t* __restrict__ idx, int n, bool nok, int j0, int cnt) {
+  v8h p;
+  if (nok && j0 < wcap) {
+    const v8h v = *reinterpret_cast<const v8h*>(wsub + (int64_t)n * wcap + j0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = (j0 + e < cnt) ? v[e] : (_Float16)0.0f;
+  } else {
+    const float sig = nok ? SCB[n] * (1.0f / 127.0f) : 0.0f;
+    const int8_t* wrow = CB + (int64_t)(nok ? n : 0) * K;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      p[e] = (nok && j0 + e < cnt) ? half_of_f32((float)wrow[idx[j0 + e]] * sig) : (_Float16)0.0f;
+  }
+  return p;
+}
+
+// Staged outlier operands, 16-byte reads only (the row exists, j0 + 8 is
+// within the staged width and the width is a multiple of 8): values j0 ..
+// j0 + 7 of activation row m / weight row n, zero at and past cnt.
+__device__ __forceinline__ v8h outlier_a8v(const uint16_t* __restrict__ subA, int cap, int m, int j0, int cnt) {
+  const v8h v = *reinterpret_cast<const v8h*>(subA + (int64_t)m * cap + j0);
+  v8h q;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = (j0 + e < cnt) ? v[e] : (_Float16)0.0f;
+  return q;
+}
+__device__ __forceinline__ v8h outlier_w8v(const uint16_t* __restrict__ wsub, int wcap, int n, int j0, int cnt) {
+  const v8h v = *reinterpret_cast<const v8h*>(wsub + (int64_t)n * wcap + j0);
+  v8h p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = (j0 + e < cnt) ? v[e] : (_Float16)0.0f;
+  return p;
+}
+
 template <int TI, int TJ, int DT, bool OV, bool LDS_OUT = false>
 __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw, int lr, int lg, int M, int N, int K,
                                              const float* __restrict__ SCA, const int8_t* __restrict__ CB,
                                              const float* __restrict__ SCB, const uint16_t* __restrict__ subA,
-                                             int cap, const typename Elem<DT>::T* __restrict__ Asrc,
+                                             int cap, const uint16_t* __restrict__ wsub, int wcap,
+                                             const typename Elem<DT>::T* __restrict__ Asrc,
                                              const int32_t* __restrict__ idx,
                                              const int32_t* __restrict__ count,
                                              const typename Elem<DT>::T* __restrict__ bias,
@@ -105,42 +168,52 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
   }
   const int cnt = count != nullptr ? *count : 0;
 
+  // outlier product operands of one step of 16 columns: P (weights, row
+  // nw + i*32 + lr) and Q[j] (activations, row mw + j*32 + lr), columns
+  // jo + lg*8 .. +7. Steps below jvec read both from the staged copies with
+  // one 16-byte read each, requested a step ahead (across slabs too, so the
+  // next slab's first step is in flight during its dequantization); later
+  // steps gather their values one by one.
+  const int jfirst = (opan != nullptr && cnt > 0) ? 16 : 0;
+  const int jvec = min(cnt, min(wcap, (cap & 7) == 0 ? cap : 0) & ~15);
+  v8h Pn, Qn[TJ];
+  auto oload = [&](int i, int jo) {
+    const int n = nw + i * 32 + lr;
+    Pn = outlier_w8v(wsub, wcap, n < N ? n : 0, jo + lg * 8, cnt);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = mw + j * 32 + lr;
+      Qn[j] = outlier_a8v(subA, cap, m < M ? m : 0, jo + lg * 8, cnt);
+    }
+  };
+  if (jfirst < jvec) oload(0, jfirst);
+
   // one slab of TJ tiles (32 output features) at a time keeps the fp32 copy small
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
-    float sb[16];
+    float sb[16], bv[16];
     if (lsc != nullptr) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const v4f v = *reinterpret_cast<const v4f*>(lsc + LSC_SCB + nb - tn0 + i * 32 + q * 8);
+        const v4f w = *reinterpret_cast<const v4f*>(lsc + LSC_BIAS + nb - tn0 + i * 32 + q * 8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sb[4 * q + e] = v[e];
+        for (int e = 0; e < 4; ++e) {
+          sb[4 * q + e] = v[e];
+          bv[4 * q + e] = w[e];
+        }
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
         sb[r] = (n < N) ? SCB[n] : 0.0f;
-      }
-    }
-    // bias first (it joins the accumulator before the outlier product)
-    float bv[16];
-    if (lsc != nullptr) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const v4f v = *reinterpret_cast<const v4f*>(lsc + LSC_BIAS + nb - tn0 + i * 32 + q * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[4 * q + e] = v[e];
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = nb + i * 32 + (r >> 2) * 8 + (r & 3);
         bv[r] = (bias != nullptr && n < N) ? Elem<DT>::to_f32(bias[n]) : 0.0f;
       }
     }
-    // C32 * (SCA * (SCB * fl32(1/127^2))) + bias in one fused multiply-add;
-    // the scale product is exactly 1 when both scales are 127
+    // C32 * (SCA * (SCB * fl32(1/127^2))) + bias in one fused multiply-add
+    // (the bias joins the accumulator before the outlier product); the scale
+    // product is exactly 1 when both scales are 127
 #pragma unroll
     for (int r = 0; r < 16; ++r) sb[r] *= (1.0f / 16129.0f);
     v16f accf[TJ];
@@ -149,42 +222,36 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
 #pragma unroll
       for (int r = 0; r < 16; ++r) accf[j][r] = __builtin_fmaf((float)acc[i][j][r], sa[j] * sb[r], bv[r]);
 
-    // outlier columns: fp16 product accumulated into the same fp32 registers;
-    // the first 16 columns come from the LDS panels when the kernel staged them
-    int jo = 0;
-    if (opan != nullptr && cnt > 0) {
+    // outlier columns: fp16 product accumulated into the same fp32 registers,
+    // the first 16 columns from the LDS panels when the kernel staged them
+    if (jfirst == 16) {
       const v8h P = *reinterpret_cast<const v8h*>(opan + (nw - tn0 + i * 32 + lr) * 32 + lg * 16);
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const v8h Q = *reinterpret_cast<const v8h*>(opan + OPAN_Q + (mw - tm0 + j * 32 + lr) * 32 + lg * 16);
         accf[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P, Q, accf[j], 0, 0, 0);
       }
-      jo = 16;
+    }
+    int jo = jfirst;
+    for (; jo < jvec; jo += 16) {
+      const v8h P = Pn;
+      v8h Q[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) Q[j] = Qn[j];
+      if (jo + 16 < jvec) oload(i, jo + 16);
+      else if (i + 1 < TI) oload(i + 1, jfirst);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) accf[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P, Q[j], accf[j], 0, 0, 0);
     }
     for (; jo < cnt; jo += 16) {
-      v8h P, Q[TJ];
       const int n = nw + i * 32 + lr;
-      const bool nok = n < N;
-      const float sig = nok ? SCB[n] * (1.0f / 127.0f) : 0.0f;
-      const int8_t* wrow = CB + (int64_t)(nok ? n : 0) * K;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int jj = jo + lg * 8 + e;
-        P[e] = (nok && jj < cnt) ? (_Float16)((float)wrow[idx[jj]] * sig) : (_Float16)0.0f;
-      }
+      const v8h P = outlier_w8(wsub, wcap, CB, SCB, K, idx, n, n < N, jo + lg * 8, cnt);
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int m = mw + j * 32 + lr;
-        const bool mok = m < M;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jj = jo + lg * 8 + e;
-          Q[j][e] = (mok && jj < cnt) ? __builtin_bit_cast(_Float16, outlier_half<DT>(subA, cap, Asrc, K, idx, m, jj))
-                                      : (_Float16)0.0f;
-        }
+        const v8h Q = outlier_a8<DT>(subA, cap, Asrc, K, idx, m, m < M, jo + lg * 8, cnt);
+        accf[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P, Q, accf[j], 0, 0, 0);
       }
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) accf[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(P, Q[j], accf[j], 0, 0, 0);
     }
 
     // cast, store
@@ -237,11 +304,13 @@ __device__ __forceinline__ void fwd_epilogue(v16i (&acc)[TI][TJ], int mw, int nw
   }
 }
 
+
 template <int BM, int BN, int BK, int DT, bool KV, bool OV>
 __global__ __launch_bounds__(256) void k_gemm_fwd(const int8_t* __restrict__ CA, const float* __restrict__ SCA,
                                                   int M, const int8_t* __restrict__ CB,
                                                   const float* __restrict__ SCB, int N, int K,
                                                   const uint16_t* __restrict__ subA, int cap,
+                                                  const uint16_t* __restrict__ wsub, int wcap,
                                                   const typename Elem<DT>::T* __restrict__ Asrc,
                                                   const int32_t* __restrict__ idx,
                                                   const int32_t* __restrict__ count,
@@ -344,8 +413,8 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(const int8_t* __restrict__ CA,
     __syncthreads();
   }
 
-  fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * WM, n0 + wn * WN, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, Asrc,
-                               idx, count, bias, out, c32);
+  fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * WM, n0 + wn * WN, lr, lg, M, N, K, SCA, CB, SCB, subA, cap, wsub, wcap,
+                               Asrc, idx, count, bias, out, c32);
 }
 
 // Large-tile forward kernel: 256 (m) x BN (n) output tile (BN = 256, or 128
@@ -360,6 +429,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
                                                         const int8_t* __restrict__ CB,
                                                         const float* __restrict__ SCB, int N, int K,
                                                         const uint16_t* __restrict__ subA, int cap,
+                                                        const uint16_t* __restrict__ wsub, int wcap,
                                                         const typename Elem<DT>::T* __restrict__ Asrc,
                                                         const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ count,
@@ -448,26 +518,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   load_b(0);
   load_a(0);
 
-  // outlier panels (first 16 outlier columns) for the epilogue, gathered while
+  // outlier panels (first 16 outlier columns) for the epilogue, read while
   // the first operand tiles are in flight: thread t covers row t >> 1 of the
   // tile, columns 8 (t & 1) .. +7, of both panels
   char* opan = reinterpret_cast<char*>(smem) + BASE;
   int o16 = 0;
   if (count != nullptr) o16 = min(*count, 16);
   const int orow = tid >> 1, oj = (tid & 1) * 8;
-  int pbyte[8];
-  uint16_t qval[8];
-  float psc = 0.0f;
+  v8h opP = {}, opQ = {};
   if (o16 > 0) {
     const int n = n0 + orow, m = m0 + orow;
-    const bool nok = (BN == 256 || orow < BN) && n < N, mok = m < M;
-    psc = nok ? SCB[n] : 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = oj + e;
-      pbyte[e] = (nok && j < o16) ? (int)CB[(int64_t)n * K + idx[j]] : 0;
-      qval[e] = (mok && j < o16) ? outlier_half<DT>(subA, cap, Asrc, K, idx, m, j) : (uint16_t)0;
-    }
+    opP = outlier_w8(wsub, wcap, CB, SCB, K, idx, n, (BN == 256 || orow < BN) && n < N, oj, o16);
+    opQ = outlier_a8<DT>(subA, cap, Asrc, K, idx, m, m < M, oj, o16);
   }
 
   // the tile's scales and bias, likewise (thread t < 256: column n0 + t,
@@ -496,15 +558,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
     lsc[LSC_SCA + tid - 256] = sc0;
   }
   if (o16 > 0) {
-    const float sig = psc * (1.0f / 127.0f);
-    v8h P, Q;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      P[e] = (_Float16)((float)pbyte[e] * sig);
-      Q[e] = __builtin_bit_cast(_Float16, qval[e]);
-    }
-    *reinterpret_cast<v8h*>(opan + orow * 32 + oj * 2) = P;
-    *reinterpret_cast<v8h*>(opan + OPAN_Q + orow * 32 + oj * 2) = Q;
+    *reinterpret_cast<v8h*>(opan + orow * 32 + oj * 2) = opP;
+    *reinterpret_cast<v8h*>(opan + OPAN_Q + orow * 32 + oj * 2) = opQ;
   }
   __syncthreads();
   fread(0, 0, 0);
@@ -579,12 +634,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
   const char* op = o16 > 0 ? opan : nullptr;
   if constexpr (DT == DT_F32) {
     fwd_epilogue<TI, TJ, DT, OV>(acc, m0 + wm * 64, n0 + wn * (BN / 2), lr, lg, M, N, K, SCA, CB, SCB, subA, cap,
-                                 Asrc, idx, count, bias, out, c32, nullptr, m0, n0, op, lsc);
+                                 wsub, wcap, Asrc, idx, count, bias, out, c32, nullptr, m0, n0, op, lsc);
   } else {
     // output tile through LDS, stored as whole rows (of the tile's BN columns)
     char* ot = reinterpret_cast<char*>(smem);
     fwd_epilogue<TI, TJ, DT, OV, true>(acc, m0 + wm * 64, n0 + wn * (BN / 2), lr, lg, M, N, K, SCA, CB, SCB, subA,
-                                       cap, Asrc, idx, count, bias, out, c32, ot, m0, n0, op, lsc);
+                                       cap, wsub, wcap, Asrc, idx, count, bias, out, c32, ot, m0, n0, op, lsc);
     __syncthreads();
     otile_store<typename Elem<DT>::T>(ot, out, N, m0, n0, M, BN == 256 ? N : min(N, n0 + BN), wave, lane);
   }
@@ -592,7 +647,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fwd_w8(const int8_t* __restrict
 
 template <int DT, bool OV, int BN>
 static hipError_t launch_fwd_w8(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                                int N, int K, const uint16_t* subA, int cap, const void* A, const int32_t* idx,
+                                int N, int K, const uint16_t* subA, int cap, const uint16_t* wsub, int wcap,
+                                const void* A, const int32_t* idx,
                                 const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   typedef typename Elem<DT>::T T;
   // both stages (or the output tile, if larger), panels, scales
@@ -605,14 +661,15 @@ static hipError_t launch_fwd_w8(const int8_t* CA, const float* SCA, int M, const
     if (e != hipSuccess) return e;
   }
   const int tiles = ((M + 255) / 256) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap,
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, wsub, wcap,
                      static_cast<const T*>(A), idx, count, static_cast<const T*>(bias), static_cast<T*>(out), c32);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int BK, int DT, bool KV, bool OV>
 static hipError_t launch_fwd_cfg(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                                 int N, int K, const uint16_t* subA, int cap, const void* A, const int32_t* idx,
+                                 int N, int K, const uint16_t* subA, int cap, const uint16_t* wsub, int wcap,
+                                 const void* A, const int32_t* idx,
                                  const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   typedef typename Elem<DT>::T T;
   constexpr int LDK = BK + 16;
@@ -624,7 +681,7 @@ static hipError_t launch_fwd_cfg(const int8_t* CA, const float* SCA, int M, cons
     if (e != hipSuccess) return e;
   }
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap,
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, CA, SCA, M, CB, SCB, N, K, subA, cap, wsub, wcap,
                      static_cast<const T*>(A), idx, count, static_cast<const T*>(bias), static_cast<T*>(out), c32);
   return hipGetLastError();
 }
@@ -644,27 +701,31 @@ int gemm_fwd_plan(int dt, int64_t M, int64_t N, int64_t K, bool aligned) {
 
 template <int DT, bool KV, bool OV>
 static hipError_t launch_fwd_dt(const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                                int N, int K, const uint16_t* subA, int cap, const void* A, const int32_t* idx,
+                                int N, int K, const uint16_t* subA, int cap, const uint16_t* wsub, int wcap,
+                                const void* A, const int32_t* idx,
                                 const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   const int plan = gemm_fwd_plan(DT, M, N, K, KV);
   if constexpr (KV) {
     if (plan == 3)
-      return launch_fwd_w8<DT, OV, 128>(CA, SCA, M, CB, SCB, N, K, subA, cap, A, idx, count, bias, out, c32, st);
+      return launch_fwd_w8<DT, OV, 128>(CA, SCA, M, CB, SCB, N, K, subA, cap, wsub, wcap, A, idx, count, bias, out,
+                                        c32, st);
     if (plan == 2)
-      return launch_fwd_w8<DT, OV, 256>(CA, SCA, M, CB, SCB, N, K, subA, cap, A, idx, count, bias, out, c32, st);
+      return launch_fwd_w8<DT, OV, 256>(CA, SCA, M, CB, SCB, N, K, subA, cap, wsub, wcap, A, idx, count, bias, out,
+                                        c32, st);
   }
-  return launch_fwd_cfg<128, 128, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, A, idx, count, bias, out,
-                                                  c32, st);
+  return launch_fwd_cfg<128, 128, 64, DT, KV, OV>(CA, SCA, M, CB, SCB, N, K, subA, cap, wsub, wcap, A, idx, count,
+                                                  bias, out, c32, st);
 }
 
 hipError_t launch_gemm_fwd(int dt, const int8_t* CA, const float* SCA, int M, const int8_t* CB, const float* SCB,
-                           int N, int K, const uint16_t* subA, int cap, const void* Asrc, const int32_t* idx,
+                           int N, int K, const uint16_t* subA, int cap, const uint16_t* wsub, int wcap,
+                           const void* Asrc, const int32_t* idx,
                            const int32_t* count, const void* bias, void* out, int32_t* c32, hipStream_t st) {
   const bool kv = (K % 16 == 0) && ((uintptr_t)CA % 16 == 0) && ((uintptr_t)CB % 16 == 0);
   const int osz = dt == DT_F32 ? 4 : 2;
   const bool ov = (N % 4 == 0) && ((uintptr_t)out % (4 * osz) == 0) && (c32 == nullptr || (uintptr_t)c32 % 16 == 0);
 #define I8L_FWD(D, A, B) \
-  return launch_fwd_dt<D, A, B>(CA, SCA, M, CB, SCB, N, K, subA, cap, Asrc, idx, count, bias, out, c32, st)
+  return launch_fwd_dt<D, A, B>(CA, SCA, M, CB, SCB, N, K, subA, cap, wsub, wcap, Asrc, idx, count, bias, out, c32, st)
   switch (dt) {
     case DT_F32:
       if (kv) { if (ov) I8L_FWD(DT_F32, true, true); else I8L_FWD(DT_F32, true, false); }

@@ -24,7 +24,11 @@
 //                fp16 value, inv = 127 / s (IEEE division), codes =
 //                rint(fl32(x * inv)) (|code| <= 127 by construction), 0 on
 //                outlier columns, outlier values copied into the dense fp16
-//                sub-matrix.
+//                sub-matrix. In a forward, the workgroups then also write the
+//                weight's side of the outlier product (the pages' subB): the
+//                dequantized int8 weights of the first outlier columns, as
+//                dense fp16 rows, so that the GEMM epilogue never gathers
+//                single bytes of the weight once per output tile.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -295,11 +299,15 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
                                                   int cols, int tau_on, const uint32_t* __restrict__ bits,
                                                   int slabs, int8_t* __restrict__ codes, float* __restrict__ scale,
                                                   int32_t* __restrict__ idx, int idx_cap,
-                                                  int32_t* __restrict__ count, uint16_t* __restrict__ sub, int cap) {
+                                                  int32_t* __restrict__ count, uint16_t* __restrict__ sub, int cap,
+                                                  const int8_t* __restrict__ wCB, const float* __restrict__ wSCB,
+                                                  int wN, uint16_t* __restrict__ wsub, int wcap) {
 #pragma clang fp contract(off)
   typedef typename Elem<DT>::T T;
   extern __shared__ uint32_t smem_q[];
   __shared__ int wsum[4];
+  __shared__ int slist[256];   // the first wcap outlier columns (weight slice)
+  const bool wfill = wsub != nullptr && wcap > 0;
   const int nwords = (cols + 31) >> 5;
   uint32_t* smask = smem_q;
   int32_t* sprefix = reinterpret_cast<int32_t*>(smem_q + nwords);
@@ -382,11 +390,12 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
       if (w >= nwords) break;
       sprefix[w] = run;
       uint32_t mw = smask[w];
-      if (blockIdx.x == 0) {
+      if (blockIdx.x == 0 || (wfill && run < wcap)) {
         int j = run;
         while (mw) {
           const int b = __ffs(mw) - 1;
-          if (j < idx_cap) idx[j] = w * 32 + b;
+          if (blockIdx.x == 0 && j < idx_cap) idx[j] = w * 32 + b;
+          if (wfill && j < wcap) slist[j] = w * 32 + b;
           ++j;
           mw &= mw - 1u;
         }
@@ -583,6 +592,35 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
       if (lane == 0) scale[row] = sv;
     }
   }
+
+  // the weight's outlier slice: four weight rows per wave and pass, lanes over
+  // the outlier columns (one byte gather each, every row's values written as
+  // one contiguous run)
+  if (tau_on && wfill) {
+    const int tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    const int cw = min(tot, wcap);
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wid, nwv = (int64_t)gridDim.x * 4;
+    for (int jb = 0; jb < cw; jb += 64) {
+      const int j = jb + lane;
+      const bool jok = j < cw;
+      const int col = jok ? slist[j] : 0;
+      for (int64_t n = gw * 4; n < wN; n += nwv * 4) {
+        int v[4];
+        float sg[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool ok = n + u < wN;
+          v[u] = (ok && jok) ? (int)wCB[(n + u) * (int64_t)cols + col] : 0;
+          sg[u] = ok ? wSCB[n + u] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (jok && n + u < wN)
+            wsub[(n + u) * (int64_t)wcap + j] =
+                __builtin_bit_cast(uint16_t, half_of_f32((float)v[u] * (sg[u] * (1.0f / 127.0f))));
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -599,7 +637,8 @@ size_t quant_scratch_words(int64_t rows, int64_t cols) {
 template <int DT>
 static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, float tau, int8_t* codes,
                                     float* scale, int32_t* idx, int idx_cap, int32_t* count, uint16_t* sub, int cap,
-                                    uint32_t* scratch, const uint32_t* preflags, hipStream_t st) {
+                                    uint32_t* scratch, const uint32_t* preflags, const OutlierWeights* ow,
+                                    hipStream_t st) {
   typedef typename Elem<DT>::T T;
   const T* X = static_cast<const T*>(Xv);
   // column flags handed over by the producer of X replace the flags pass
@@ -619,6 +658,14 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
   // workgroups: four rows at a time (one per wave), or one row at a time
   const int64_t rblocks = rows > 0 ? ((rows + 3) / 4 < RQ_MAX_BLOCKS ? (rows + 3) / 4 : RQ_MAX_BLOCKS) : 1;
   const int64_t wblocks = rows > 0 ? (rows < RQ_MAX_BLOCKS ? rows : RQ_MAX_BLOCKS) : 1;
+  // with the weight slice to write, at least one wave per 16 weight rows (up
+  // to the cap); the extra workgroups have no rows of X
+  const bool wf = ow != nullptr && ow->wsub != nullptr && ow->wcap > 0 && ow->N > 0 && tau_on;
+  const int64_t fblocks = wf ? ((int64_t)ow->N + 15) / 16 : 1;
+  const int8_t* wCB = wf ? ow->CB : nullptr;
+  const float* wSCB = wf ? ow->SCB : nullptr;
+  uint16_t* wsub = wf ? ow->wsub : nullptr;
+  const int wN = wf ? ow->N : 0, wcap = wf ? ow->wcap : 0;
   const int nchunk = (cols + 7) / 8;
   const size_t lds = tau_on ? (size_t)2 * (nwords > 0 ? nwords : 1) * 4 : 0;
 #define I8L_RQ(NCH, VEC, WGM)                                                                                   \
@@ -628,9 +675,10 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
       hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (e != hipSuccess) return e;                                                                            \
     }                                                                                                           \
-    const int64_t nb = WGM ? wblocks : rblocks;                                                                 \
+    int64_t nb = WGM ? wblocks : rblocks;                                                                       \
+    if (fblocks > nb) nb = fblocks < RQ_MAX_BLOCKS ? fblocks : RQ_MAX_BLOCKS;                                   \
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(256), lds, st, X, rows, cols, (int)tau_on, bits, slabs,   \
-                       codes, scale, idx, idx_cap, count, sub, cap);                                            \
+                       codes, scale, idx, idx_cap, count, sub, cap, wCB, wSCB, wN, wsub, wcap);                 \
   } while (0)
   // 16-bit rows stay in registers between the absmax and the quantization:
   // rows of up to 4096 values in one wave, up to 32768 values spread over a
@@ -662,18 +710,19 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
 
 hipError_t launch_quantize(int dt, const void* X, int64_t rows, int cols, float tau, int8_t* codes, float* scale,
                            int32_t* idx, int32_t* count, uint16_t* sub, int cap, uint32_t* scratch,
-                           hipStream_t st, const uint32_t* preflags, int idx_cap) {
+                           hipStream_t st, const uint32_t* preflags, int idx_cap, const OutlierWeights* ow) {
   if (idx_cap < 0) idx_cap = cap;
+  if (ow != nullptr && (ow->K != cols || ow->wcap > 256)) return hipErrorInvalidValue;
   switch (dt) {
     case DT_F32:
       return launch_quantize_t<DT_F32>(X, rows, cols, tau, codes, scale, idx, idx_cap, count, sub, cap, scratch,
-                                       preflags, st);
+                                       preflags, ow, st);
     case DT_F16:
       return launch_quantize_t<DT_F16>(X, rows, cols, tau, codes, scale, idx, idx_cap, count, sub, cap, scratch,
-                                       preflags, st);
+                                       preflags, ow, st);
     default:
       return launch_quantize_t<DT_BF16>(X, rows, cols, tau, codes, scale, idx, idx_cap, count, sub, cap, scratch,
-                                        preflags, st);
+                                        preflags, ow, st);
   }
 }
 

@@ -94,7 +94,7 @@ def test_quantize_host_errors(L):
 def test_forward_host_errors(L):
     f = L.lib.int8_linear_forward
     M, K, N, cap = 8, 64, 32, 64
-    ws = L.lib.int8_linear_forward_workspace_bytes(M, K, cap)
+    ws = L.lib.int8_linear_forward_workspace_bytes(M, K, N, cap)
     base = dict(A=FAKE, dt=1, M=M, K=K, CB=FAKE, SCB=FAKE, N=N, bias=0, tau=6.0, cap=cap, out=FAKE, c32=0, ws=FAKE,
                 wsb=ws, st=None)
 
@@ -117,7 +117,7 @@ def test_forward_host_errors(L):
     assert call(wsb=ws - 1) == L.I8L_EWORKSPACE
     assert call(ws=FAKE + 16) == L.I8L_EINVAL
     # empty problems succeed without touching the device
-    assert call(M=0, wsb=L.lib.int8_linear_forward_workspace_bytes(0, K, cap)) == L.I8L_OK
+    assert call(M=0, wsb=L.lib.int8_linear_forward_workspace_bytes(0, K, N, cap)) == L.I8L_OK
     assert call(N=0) == L.I8L_OK
 
 
@@ -210,7 +210,7 @@ def test_producer_flags_host_errors(L):
     assert words(-1, 8) == 0
     g = L.lib.int8_linear_forward_flagged
     M, K, N = 8, 64, 32
-    wsb = L.lib.int8_linear_forward_workspace_bytes(M, K, K)
+    wsb = L.lib.int8_linear_forward_workspace_bytes(M, K, N, K)
     base = dict(A=FAKE, dt=2, M=M, K=K, fl=FAKE, fw=words(M, K), CB=FAKE, SCB=FAKE, N=N, b=None, cap=K, out=FAKE,
                 c32=None, ws=FAKE, wsb=wsb, st=None)
 
@@ -226,24 +226,36 @@ def test_producer_flags_host_errors(L):
     assert call(K=L.I8L_MAX_K + 1, wsb=1 << 40) == L.I8L_ESHAPE
 
 
+def wsub_width(cap):
+    """Columns of the weight's dequantized outlier slice for staging width cap:
+    cap rounded up to a multiple of 8, at most 256."""
+    return 0 if cap <= 0 else min((cap + 7) // 8 * 8, 256)
+
+
 def test_forward_layout(L):
-    for (M, K, cap) in [(1, 1, 0), (600, 4, 4), (2048, 4096, 4096), (16384, 28672, 28672), (5, 70, 3)]:
+    for (M, K, N, cap) in [(1, 1, 1, 0), (600, 4, 9, 4), (2048, 4096, 11008, 4096), (16384, 28672, 8192, 28672),
+                           (5, 70, 3, 3), (7, 64, 0, 17)]:
         lay = L.ForwardLayout()
-        assert L.lib.int8_linear_forward_workspace_layout(M, K, cap, lay) == 0
-        offs = [lay.count, lay.idx, lay.scale, lay.codes, lay.sub]
-        sizes = [4, 4 * K, 4 * M, M * K, 2 * M * cap]
+        assert L.lib.int8_linear_forward_workspace_layout(M, K, N, cap, lay) == 0
+        offs = [lay.count, lay.idx, lay.scale, lay.codes, lay.sub, lay.wsub]
+        sizes = [4, 4 * K, 4 * M, M * K, 2 * M * cap, 2 * N * wsub_width(cap)]
         assert all(o % 256 == 0 for o in offs)
         for (o, s), o2 in zip(zip(offs, sizes), offs[1:] + [lay.total]):
             assert o + s <= o2
-        assert lay.total == L.lib.int8_linear_forward_workspace_bytes(M, K, cap)
-    assert L.lib.int8_linear_forward_workspace_layout(-1, 4, 4, L.ForwardLayout()) == L.I8L_EINVAL
-    # the outlier list always has room for every column; only the staging width follows cap
+        assert lay.total == L.lib.int8_linear_forward_workspace_bytes(M, K, N, cap)
+    assert [wsub_width(c) for c in (0, 1, 8, 9, 16, 17, 255, 256, 257, 4096)] == [0, 8, 8, 16, 16, 24, 256, 256,
+                                                                                   256, 256]
+    assert L.lib.int8_linear_forward_workspace_layout(-1, 4, 4, 4, L.ForwardLayout()) == L.I8L_EINVAL
+    assert L.lib.int8_linear_forward_workspace_layout(4, 4, -1, 4, L.ForwardLayout()) == L.I8L_EINVAL
+    assert L.lib.int8_linear_forward_workspace_bytes(4, 4, -1, 4) == 0
+    # the outlier list always has room for every column; only the staging widths follow cap
     small, big = L.ForwardLayout(), L.ForwardLayout()
-    L.lib.int8_linear_forward_workspace_layout(16384, 28672, 256, small)
-    L.lib.int8_linear_forward_workspace_layout(16384, 28672, 28672, big)
+    L.lib.int8_linear_forward_workspace_layout(16384, 28672, 8192, 256, small)
+    L.lib.int8_linear_forward_workspace_layout(16384, 28672, 8192, 28672, big)
     assert small.sub - small.idx >= 4 * 28672
-    assert small.total < 16384 * 28672 + 2 * 16384 * 256 + (1 << 20)
+    assert small.total < 16384 * 28672 + 2 * (16384 + 8192) * 256 + (1 << 20)
     assert big.total - small.total >= 2 * 16384 * (28672 - 256)
+    assert big.total - big.wsub < 2 * 8192 * 256 + (1 << 16)   # the weight slice stays at 256 columns
 
 
 def test_gemm_dispatch(L):
@@ -310,11 +322,11 @@ def test_noalloc_forward_host_errors(L):
     cap_max = L.lib.int8_linear_forward_noalloc_max_bytes()
     assert cap_max == L.I8L_NOALLOC_SCRATCH_BYTES == 64 << 20
     need = L.lib.int8_linear_forward_noalloc_bytes
-    assert need(4096, 11008) <= cap_max               # the 7B block's widest input fits
-    assert need(16384, 28672) > cap_max               # the 70B down layer does not
-    assert need(300, 1040) == L.lib.int8_linear_forward_workspace_bytes(300, 1040, 64)
-    assert need(5, 16) == L.lib.int8_linear_forward_workspace_bytes(5, 16, 16)
-    assert need(-1, 4) == 0
+    assert need(4096, 11008, 4096) <= cap_max         # the 7B block's widest input fits
+    assert need(16384, 28672, 8192) > cap_max         # the 70B down layer does not
+    assert need(300, 1040, 77) == L.lib.int8_linear_forward_workspace_bytes(300, 1040, 77, 64)
+    assert need(5, 16, 3) == L.lib.int8_linear_forward_workspace_bytes(5, 16, 3, 16)
+    assert need(-1, 4, 4) == 0 and need(4, 4, -1) == 0
     base = dict(A=FAKE, dt=2, M=8, K=64, CB=FAKE, SCB=FAKE, N=32, b=None, tau=6.0, out=FAKE, st=None)
 
     def call(**kw):

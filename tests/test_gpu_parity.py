@@ -130,11 +130,16 @@ def _check_weights(I8, W):
     return CB, SCB, cb, scb
 
 
+def wsub_width(cap):
+    """Columns of the weight's outlier slice for staging width cap (a multiple of 8, at most 256)."""
+    return 0 if cap <= 0 else min((cap + 7) // 8 * 8, 256)
+
+
 def _forward_and_check(I8, A, dt, CB, SCB, cb, scb, bias, tau, cap=None, rows=None):
     M, K = A.shape
     N = cb.shape[0]
     capn = K if cap is None else cap
-    ws = I8.forward_workspace(M, K, capn, "cuda:0")
+    ws = I8.forward_workspace(M, K, N, capn, "cuda:0")
     ws.fill_(0x5C)                   # arbitrary bytes: workspaces need no initialisation
     c32 = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
     Ad, bd = dev(A, dt), (dev(bias, dt) if bias is not None else None)
@@ -145,7 +150,7 @@ def _forward_and_check(I8, A, dt, CB, SCB, cb, scb, bias, tau, cap=None, rows=No
     f = oracle.linear_forward(A, dt, cb, scb, bias, tau, rows=rows)
     q = f["q"]
     # the forward's own quantization, read back from its workspace
-    L = I8.forward_layout(M, K, capn)
+    L = I8.forward_layout(M, K, N, capn)
     wsh = host(ws)
     cnt = int(wsh[L.count:L.count + 4].view(np.int32)[0])
     assert cnt == q["outliers"].size
@@ -157,6 +162,12 @@ def _forward_and_check(I8, A, dt, CB, SCB, cb, scb, bias, tau, cap=None, rows=No
     if capn:
         subw = wsh[L.sub:L.sub + 2 * M * capn].view(np.float16).reshape(M, capn)[:, :k]
         assert_bits_equal(subw, q["sub"][:, :k], "subA")
+    # the weight's dequantized outlier slice written by the row pass
+    wcap = wsub_width(capn)
+    kw = min(cnt, wcap)
+    if kw:
+        wsw = wsh[L.wsub:L.wsub + 2 * N * wcap].view(np.float16).reshape(N, wcap)[:, :kw]
+        assert_bits_equal(wsw, oracle.dequant_weight(cb, scb, cols=q["outliers"][:kw]), "weight outlier slice")
     idx = f["rows"]
     assert_bits_equal(host(c32)[idx], f["c32"].astype(np.int32), "C32")
     assert_float_gate(host(out)[idx], dt, f["y"], "out")
@@ -291,9 +302,34 @@ def test_forward_outliers_beyond_staging(I8, dt, M, K, N):
         outs[cap] = host(out)
     for cap in (0, 2, 16, 17):       # identical bits whatever the staging width
         assert_bits_equal(outs[cap], outs[K], f"out with cap={cap} against cap=K")
-    ws = I8.forward_workspace(M, K, 3, "cuda:0")
+    ws = I8.forward_workspace(M, K, N, 3, "cuda:0")
     I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt), 6.0, cap=3, workspace=ws)
-    assert I8.forward_check(ws, M, K, 3) == f["q"]["outliers"].size
+    assert I8.forward_check(ws, M, K, N, 3) == f["q"]["outliers"].size
+
+
+# many outlier columns (150 and 300, beyond the 256-column staging): the
+# generic kernel and both large-tile kernels, with the default staging width
+# (16-byte staged reads up to 256 columns, gathered values beyond) and with a
+# staging width that is not a multiple of 8 (every value gathered); the bits
+# must not depend on it
+MSHAPES = [(300, 1040, 520), (2100, 1040, 2090), (1040, 512, 8320)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("M,K,N", MSHAPES)
+@pytest.mark.parametrize("n_out", [150, 300])
+def test_forward_many_outliers(I8, dt, M, K, N, n_out):
+    A, W, b, _ = _layer(dt, M, K, N, 9, n_out=n_out)
+    CB, SCB, cb, scb = _check_weights(I8, W)
+    rows = np.unique(np.concatenate([np.arange(0, M, 61), [M - 1, 255, 256, 257]]))
+    outs = {}
+    for cap in (None, 100):
+        print(f"  [{dt} {M}x{K}x{N}] outliers={n_out} cap={cap}", flush=True)
+        out, f = _forward_and_check(I8, A, dt, CB, SCB, cb, scb, b, 6.0, cap=I8.default_cap(K) if cap is None
+                                    else cap, rows=rows)
+        assert f["q"]["outliers"].size >= n_out
+        outs[cap] = host(out)
+    assert_bits_equal(outs[100], outs[None], "out with cap=100 against the default staging")
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])

@@ -82,7 +82,7 @@ def test_flagged_forward_equals_forward(I8, dt, M, K, N):
     CB, SCB = I8.quantize_weight(dev(c["W"]))
     b = dev(c["bias"], dt)
     A, flags = I8.silu_outlier_flags(dev(H, dt), 6.0)
-    ws1, ws2 = I8.forward_workspace(M, K, K, "cuda:0"), I8.forward_workspace(M, K, K, "cuda:0")
+    ws1, ws2 = I8.forward_workspace(M, K, N, K, "cuda:0"), I8.forward_workspace(M, K, N, K, "cuda:0")
     c1 = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
     c2 = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
     o1 = I8.int8_linear_forward(A, CB, SCB, b, 6.0, K, c32=c1, workspace=ws1)
@@ -90,7 +90,7 @@ def test_flagged_forward_equals_forward(I8, dt, M, K, N):
     torch.cuda.synchronize()
     assert_bits_equal(host(c2), host(c1), "C32")
     assert_bits_equal(host(o2), host(o1), "out")
-    lay = I8.forward_layout(M, K, K)
+    lay = I8.forward_layout(M, K, N, K)
     cnt = int(host(ws1[lay.count:lay.count + 4]).view(np.int32)[0])
     assert cnt >= 1
     # the outlier list holds `count` entries; the rest of its buffer is not written
@@ -157,9 +157,9 @@ def test_flagged_forward_beyond_staging(I8):
     H = _H("f16", M, K, 5, hot=6)
     A, flags = I8.silu_outlier_flags(dev(H, "f16"), 6.0)
     CB, SCB = I8.quantize_weight(torch.randn(N, K, device="cuda:0") * 0.02)
-    ws = I8.forward_workspace(M, K, 2, "cuda:0")
+    ws = I8.forward_workspace(M, K, N, 2, "cuda:0")
     o2 = I8.int8_linear_forward_flagged(A, flags, CB, SCB, None, cap=2, workspace=ws)
-    assert I8.forward_check(ws, M, K, 2) >= 6
+    assert I8.forward_check(ws, M, K, N, 2) >= 6
     oK = I8.int8_linear_forward_flagged(A, flags, CB, SCB, None, cap=K)
     oP = I8.int8_linear_forward(A, CB, SCB, None, 6.0, cap=K)
     torch.cuda.synchronize()

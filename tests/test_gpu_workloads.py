@@ -48,7 +48,7 @@ def test_workload_layer(I8, name, li):
     b = workloads.make_bias(wl, li)
     M, K, N = L.M, L.K, L.N
     cap = I8.default_cap(K)
-    ws = I8.forward_workspace(M, K, cap, "cuda:0")
+    ws = I8.forward_workspace(M, K, N, cap, "cuda:0")
     c32 = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
     out = I8.int8_linear_forward(dev(A, dt), CB, SCB, dev(b, dt) if b is not None else None, tau, cap, c32=c32,
                                  workspace=ws)
@@ -57,7 +57,7 @@ def test_workload_layer(I8, name, li):
     print("  forward done on GPU; oracle ...", flush=True)
     f = oracle.linear_forward(A, dt, cb, scb, b, tau, rows=rows)
     q = f["q"]
-    lay = I8.forward_layout(M, K, cap)
+    lay = I8.forward_layout(M, K, N, cap)
     cnt = int(host(ws[lay.count:lay.count + 4]).view(np.int32)[0])
     assert cnt == q["outliers"].size
     seeded = workloads.outlier_columns(wl.wid, li, K, L.n_outliers)

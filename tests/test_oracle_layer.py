@@ -256,6 +256,23 @@ def test_dequant_constant_is_one_for_scale_127():
     assert np.float32(127) * (np.float32(1) / np.float32(127)) == np.float32(1.0)
 
 
+def test_dequant_weight_rounds_twice_at_an_fp16_midpoint():
+    """Reading 9 rounds CB * sigma to fp32, then to fp16. With SCB = 0x41cb4c9a
+    (25.41240...), 5 * sigma = 1.00048832... exactly, 4.5e-8 above the fp16
+    midpoint 1 + 2^-11; the fp32 spacing at 1 is 2^-23, so the fp32 product is
+    that midpoint, which ties to the even neighbour 1.0 (0x3C00). Rounding the
+    exact product once would give 1 + 2^-10 (0x3C01). Likewise 10 * sigma lands
+    on 2 + 2^-10 and ties to 2.0 (0x4000)."""
+    scb = np.array([0x41CB4C9A], np.uint32).view(np.float32)
+    sig = fl32(Fraction(float(scb[0])) * INV127)
+    exact = 5 * sig
+    mid = 1 + Fraction(1, 2048)
+    assert exact > mid and fl32(exact) == mid                       # the worked case holds
+    assert exact_round(exact, "f16") == 1 + Fraction(1, 1024)       # one rounding: the other neighbour
+    w = oracle.dequant_weight(np.array([[5, -5, 0, 10, -10]], np.int8), scb)
+    assert w.view(np.uint16)[0].tolist() == [0x3C00, 0xBC00, 0x0000, 0x4000, 0xC000]
+
+
 # --------------------------------------------------------------------------
 # brute force of the whole forward / backward on tiny inputs
 

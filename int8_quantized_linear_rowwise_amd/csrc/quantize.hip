@@ -29,6 +29,7 @@
 //                dequantized int8 weights of the first outlier columns, as
 //                dense fp16 rows, so that the GEMM epilogue never gathers
 //                single bytes of the weight once per output tile.
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -275,6 +276,195 @@ __global__ __launch_bounds__(256) void k_colflags(const typename Elem<DT>::T* __
 }
 
 // ---------------------------------------------------------------------------
+// Per-chunk pieces of the row kernels (a chunk: 8 consecutive columns).
+
+// column-mask bits of chunk ci
+__device__ __forceinline__ uint32_t chunk_mask_bits(const uint32_t* smask, int ci) {
+  const int c0 = ci * 8;
+  return (smask[c0 >> 5] >> (c0 & 31)) & 0xffu;
+}
+
+// largest magnitude (storage-format bits) of the chunk's non-outlier
+// elements; om: the chunk's outlier-column bits; any: some lane of the wave
+// has an outlier column in this chunk (wave-uniform, so that the common case
+// skips all masking)
+template <int DT, bool VEC>
+__device__ __forceinline__ uint32_t chunk_absmax(const v4u& a, const v4u& b, uint32_t om, bool any) {
+  if constexpr (VEC && DT != DT_F32) {
+    us2 mx = {0, 0};
+    if (!any) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, a[d] & 0x7fff7fffu));
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t keep = (((om >> (2 * d)) & 1u) ? 0u : 0x0000ffffu) | (((om >> (2 * d + 1)) & 1u) ? 0u : 0xffff0000u);
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, a[d] & 0x7fff7fffu & keep));
+      }
+    }
+    return max((uint32_t)mx[0], (uint32_t)mx[1]);
+  } else {
+    uint32_t mx = 0u;
+    if (!any) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = max(mx, chunk_mag<DT>(a, b, e));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t m = chunk_mag<DT>(a, b, e);
+        mx = ((om >> e) & 1u) ? mx : max(mx, m);
+      }
+    }
+    return mx;
+  }
+}
+
+// codes of one chunk, packed little-endian into two words: x16 = fp16(x),
+// code = rint(fl32(x16 * inv)) by the exact fp32 add of 1.5 * 2^23
+template <int DT>
+__device__ __forceinline__ void chunk_quant8(const v4u& a, const v4u& b, float inv, uint32_t& lo, uint32_t& hi) {
+#pragma clang fp contract(off)
+  uint32_t h[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if constexpr (DT == DT_F16) h[d] = a[d];
+    else if constexpr (DT == DT_BF16) h[d] = bf16x2_to_f16x2(a[d]);
+    else h[d] = f32x2_to_f16x2(__uint_as_float(d < 2 ? a[2 * d] : b[2 * d - 4]),
+                               __uint_as_float(d < 2 ? a[2 * d + 1] : b[2 * d - 3]));
+  }
+  uint32_t q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)(h[e >> 1] >> (16 * (e & 1))));
+    const float p = (float)x * inv;
+    q[e] = __float_as_uint(p + 12582912.0f);
+  }
+  lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u) | __builtin_amdgcn_perm(q[3], q[2], 0x04000c0cu);
+  hi = __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u) | __builtin_amdgcn_perm(q[7], q[6], 0x04000c0cu);
+}
+
+// chunk ci of row `row` to memory: codes, 0 on outlier columns, whose fp16
+// values go to the dense sub-matrix at their rank among the outlier columns
+// (the prefix of the column's mask word plus the set bits below it)
+template <int DT, bool VEC>
+__device__ __forceinline__ void chunk_emit(int8_t* __restrict__ codes, uint16_t* __restrict__ sub, int cap,
+                                           int cols, const uint32_t* smask, const int32_t* sprefix, int64_t row,
+                                           int ci, const v4u& a, const v4u& b, float inv, uint32_t om, bool any) {
+  const int c0 = ci * 8;
+  uint32_t lo, hi;
+  chunk_quant8<DT>(a, b, inv, lo, hi);
+  if (any && om) {
+    uint32_t kl = 0u, kh = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kl |= ((om >> e) & 1u) ? 0u : (0xffu << (8 * e));
+      kh |= ((om >> (e + 4)) & 1u) ? 0u : (0xffu << (8 * e));
+    }
+    lo &= kl;
+    hi &= kh;
+    uint16_t* srow = sub + row * (int64_t)cap;
+    const int w = c0 >> 5;
+    const uint32_t mw = smask[w];
+    const int base = sprefix[w];
+    uint32_t rest = om;
+    while (rest) {
+      const int e = __ffs(rest) - 1;
+      rest &= rest - 1u;
+      const int c = c0 + e;
+      const int j = base + __popc(mw & ((1u << (c & 31)) - 1u));
+      if (j < cap) srow[j] = __builtin_bit_cast(uint16_t, (_Float16)chunk_val<DT>(a, b, e));
+    }
+  }
+  int8_t* cr = codes + row * (int64_t)cols + c0;
+  if constexpr (VEC) {
+    *reinterpret_cast<v2u*>(cr) = v2u{lo, hi};
+  } else {
+    for (int e = 0; e < 8; ++e)
+      if (c0 + e < cols) cr[e] = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xffu);
+  }
+}
+
+// With the column mask in LDS (smask, written by the whole workgroup and
+// followed by a barrier): the exclusive popcount prefix per word (sprefix,
+// LDS). With `list`, the ascending outlier list (first idx_cap entries) and
+// the count go to memory; the first wcap columns also go to slist (LDS).
+// Called by the whole workgroup; returns |O|.
+__device__ __forceinline__ int mask_prefix(const uint32_t* smask, int32_t* sprefix, int* wsum, int nwords,
+                                           bool list, int32_t* __restrict__ idx, int idx_cap,
+                                           int32_t* __restrict__ count, int* slist, int wcap) {
+  const int t = threadIdx.x, lane = t & 63, wid = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int per = (nwords + 255) / 256;
+  const int w0 = t * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (w0 + i < nwords) local += __popc(smask[w0 + i]);
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int i = 0; i < wid; ++i) run += wsum[i];
+  for (int i = 0; i < per; ++i) {
+    const int w = w0 + i;
+    if (w >= nwords) break;
+    sprefix[w] = run;
+    uint32_t mw = smask[w];
+    if (list || run < wcap) {
+      int j = run;
+      while (mw) {
+        const int b = __ffs(mw) - 1;
+        if (list && j < idx_cap) idx[j] = w * 32 + b;
+        if (j < wcap) slist[j] = w * 32 + b;
+        ++j;
+        mw &= mw - 1u;
+      }
+    }
+    run += __popc(smask[w]);
+  }
+  const int tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  if (list && t == 0) *count = tot;
+  __syncthreads();
+  return tot;
+}
+
+// The weight's side of the outlier product in a forward: wsub[n * wcap + j] =
+// fp16(fl32(CB[n, O[j]] * fl32(SCB[n] * fl32(1/127)))) for j < min(tot, wcap),
+// the columns listed in slist. Four weight rows per wave and pass, lanes over
+// the outlier columns (one byte gather each, every row's values written as
+// one contiguous run).
+__device__ __forceinline__ void weight_slice(const int8_t* __restrict__ wCB, const float* __restrict__ wSCB, int wN,
+                                             int K, uint16_t* __restrict__ wsub, int wcap, const int* slist,
+                                             int tot) {
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cw = min(tot, wcap);
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wid, nwv = (int64_t)gridDim.x * 4;
+  for (int jb = 0; jb < cw; jb += 64) {
+    const int j = jb + lane;
+    const bool jok = j < cw;
+    const int col = jok ? slist[j] : 0;
+    for (int64_t n = gw * 4; n < wN; n += nwv * 4) {
+      int v[4];
+      float sg[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = n + u < wN;
+        v[u] = (ok && jok) ? (int)wCB[(n + u) * (int64_t)K + col] : 0;
+        sg[u] = ok ? wSCB[n + u] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (jok && n + u < wN)
+          wsub[(n + u) * (int64_t)wcap + j] =
+              __builtin_bit_cast(uint16_t, half_of_f32((float)v[u] * (sg[u] * (1.0f / 127.0f))));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Row quantization. Prologue of every workgroup (tau on): column mask = OR
 // of the slab words, exclusive per-word popcount prefix, both in LDS;
 // workgroup 0 writes the ascending outlier list (first cap entries) and the
@@ -334,8 +524,6 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
 #pragma unroll
     for (int sl = 0; sl < CF_MAX_SLABS; ++sl) sw[sl] = sl < slabs ? bits[(int64_t)sl * nwords + t] : 0u;
   }
-  // the first row of a register-resident wave is requested before the
-  // prologue, so that its memory latency overlaps the mask construction
   // register-resident rows (16-bit, VEC) are read through a buffer resource
   // per row: chunks past the row read as zero without a memory access, so the
   // loads need no branch. The first row is requested before the prologue, so
@@ -353,6 +541,7 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
   };
   if constexpr (NCH > 0) load_row(row0, ra);
 
+  int tot = 0;
   if (tau_on) {
     if (w0ok) {
       uint32_t mw = 0u;
@@ -370,136 +559,18 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
       smask[w] = mw;
     }
     __syncthreads();
-    const int per = (nwords + 255) / 256;
-    const int w0 = t * per;
-    int local = 0;
-    for (int i = 0; i < per; ++i)
-      if (w0 + i < nwords) local += __popc(smask[w0 + i]);
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
-    if (lane == 63) wsum[wid] = incl;
-    __syncthreads();
-    int run = incl - local;
-    for (int i = 0; i < wid; ++i) run += wsum[i];
-    for (int i = 0; i < per; ++i) {
-      const int w = w0 + i;
-      if (w >= nwords) break;
-      sprefix[w] = run;
-      uint32_t mw = smask[w];
-      if (blockIdx.x == 0 || (wfill && run < wcap)) {
-        int j = run;
-        while (mw) {
-          const int b = __ffs(mw) - 1;
-          if (blockIdx.x == 0 && j < idx_cap) idx[j] = w * 32 + b;
-          if (wfill && j < wcap) slist[j] = w * 32 + b;
-          ++j;
-          mw &= mw - 1u;
-        }
-      }
-      run += __popc(smask[w]);
-    }
-    if (blockIdx.x == 0 && t == 0) *count = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
+    tot = mask_prefix(smask, sprefix, wsum, nwords, blockIdx.x == 0, idx, idx_cap, count, slist,
+                      wfill ? wcap : 0);
   } else if (blockIdx.x == 0 && t == 0) {
     *count = 0;
   }
 
-  auto chunk_mask = [&](int ci) -> uint32_t {
-    if (!tau_on) return 0u;
-    const int c0 = ci * 8;
-    return (smask[c0 >> 5] >> (c0 & 31)) & 0xffu;
-  };
-  // largest magnitude (storage-format bits) of the chunk's non-outlier elements;
-  // any: some lane of the wave has an outlier column in this chunk (uniform)
+  auto chunk_mask = [&](int ci) -> uint32_t { return tau_on ? chunk_mask_bits(smask, ci) : 0u; };
   auto absmax = [&](const v4u& a, const v4u& b, uint32_t om, bool any) -> uint32_t {
-    if constexpr (VEC && DT != DT_F32) {
-      us2 mx = {0, 0};
-      if (!any) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, a[d] & 0x7fff7fffu));
-      } else {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t keep = (((om >> (2 * d)) & 1u) ? 0u : 0x0000ffffu) | (((om >> (2 * d + 1)) & 1u) ? 0u : 0xffff0000u);
-          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, a[d] & 0x7fff7fffu & keep));
-        }
-      }
-      return max((uint32_t)mx[0], (uint32_t)mx[1]);
-    } else {
-      uint32_t mx = 0u;
-      if (!any) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = max(mx, chunk_mag<DT>(a, b, e));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t m = chunk_mag<DT>(a, b, e);
-          mx = ((om >> e) & 1u) ? mx : max(mx, m);
-        }
-      }
-      return mx;
-    }
-  };
-  // codes of one chunk, packed little-endian into two words
-  auto quant8 = [&](const v4u& a, const v4u& b, float inv, uint32_t& lo, uint32_t& hi) {
-    uint32_t h[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      if constexpr (DT == DT_F16) h[d] = a[d];
-      else if constexpr (DT == DT_BF16) h[d] = bf16x2_to_f16x2(a[d]);
-      else h[d] = f32x2_to_f16x2(__uint_as_float(d < 2 ? a[2 * d] : b[2 * d - 4]),
-                                 __uint_as_float(d < 2 ? a[2 * d + 1] : b[2 * d - 3]));
-    }
-    uint32_t q[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)(h[e >> 1] >> (16 * (e & 1))));
-      const float p = (float)x * inv;
-      q[e] = __float_as_uint(p + 12582912.0f);
-    }
-    lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u) | __builtin_amdgcn_perm(q[3], q[2], 0x04000c0cu);
-    hi = __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u) | __builtin_amdgcn_perm(q[7], q[6], 0x04000c0cu);
+    return chunk_absmax<DT, VEC>(a, b, om, any);
   };
   auto emit = [&](int64_t row, int ci, const v4u& a, const v4u& b, float inv, uint32_t om, bool any) {
-    const int c0 = ci * 8;
-    uint32_t lo, hi;
-    quant8(a, b, inv, lo, hi);
-    if (any && om) {
-      // outlier columns: code 0 (byte mask), value to the dense sub-matrix
-      uint32_t kl = 0u, kh = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kl |= ((om >> e) & 1u) ? 0u : (0xffu << (8 * e));
-        kh |= ((om >> (e + 4)) & 1u) ? 0u : (0xffu << (8 * e));
-      }
-      lo &= kl;
-      hi &= kh;
-      // rank of column c among the outlier columns: prefix of its word plus the
-      // set bits below it
-      uint16_t* srow = sub + row * (int64_t)cap;
-      const int w = c0 >> 5;
-      const uint32_t mw = smask[w];
-      const int base = sprefix[w];
-      uint32_t rest = om;
-      while (rest) {
-        const int e = __ffs(rest) - 1;
-        rest &= rest - 1u;
-        const int c = c0 + e;
-        const int j = base + __popc(mw & ((1u << (c & 31)) - 1u));
-        if (j < cap) srow[j] = __builtin_bit_cast(uint16_t, (_Float16)chunk_val<DT>(a, b, e));
-      }
-    }
-    int8_t* cr = codes + row * (int64_t)cols + c0;
-    if constexpr (VEC) {
-      *reinterpret_cast<v2u*>(cr) = v2u{lo, hi};
-    } else {
-      for (int e = 0; e < 8; ++e)
-        if (c0 + e < cols) cr[e] = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xffu);
-    }
+    chunk_emit<DT, VEC>(codes, sub, cap, cols, smask, sprefix, row, ci, a, b, inv, om, any);
   };
   // with WG the wave maxima meet in LDS; the two slots alternate by row, so
   // one barrier per row suffices
@@ -593,34 +664,7 @@ __global__ __launch_bounds__(256) void k_rowquant(const typename Elem<DT>::T* __
     }
   }
 
-  // the weight's outlier slice: four weight rows per wave and pass, lanes over
-  // the outlier columns (one byte gather each, every row's values written as
-  // one contiguous run)
-  if (tau_on && wfill) {
-    const int tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    const int cw = min(tot, wcap);
-    const int64_t gw = (int64_t)blockIdx.x * 4 + wid, nwv = (int64_t)gridDim.x * 4;
-    for (int jb = 0; jb < cw; jb += 64) {
-      const int j = jb + lane;
-      const bool jok = j < cw;
-      const int col = jok ? slist[j] : 0;
-      for (int64_t n = gw * 4; n < wN; n += nwv * 4) {
-        int v[4];
-        float sg[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bool ok = n + u < wN;
-          v[u] = (ok && jok) ? (int)wCB[(n + u) * (int64_t)cols + col] : 0;
-          sg[u] = ok ? wSCB[n + u] : 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (jok && n + u < wN)
-            wsub[(n + u) * (int64_t)wcap + j] =
-                __builtin_bit_cast(uint16_t, half_of_f32((float)v[u] * (sg[u] * (1.0f / 127.0f))));
-      }
-    }
-  }
+  if (tau_on && wfill) weight_slice(wCB, wSCB, wN, cols, wsub, wcap, slist, tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -647,25 +691,26 @@ static hipError_t launch_quantize_t(const void* Xv, int64_t rows, int cols, floa
   const int nwords = (cols + 31) / 32;
   const int vec = (cols % 8 == 0) && aligned(X, 16) && aligned(codes, 8);
   const int slabs = colflag_slabs(rows, cols);
+  const uint32_t* bits = preflags != nullptr ? preflags : scratch;
+  // weight slice (forward only)
+  const bool wf = ow != nullptr && ow->wsub != nullptr && ow->wcap > 0 && ow->N > 0 && tau_on;
+  const int8_t* wCB = wf ? ow->CB : nullptr;
+  const float* wSCB = wf ? ow->SCB : nullptr;
+  uint16_t* wsub = wf ? ow->wsub : nullptr;
+  const int wN = wf ? ow->N : 0, wcap = wf ? ow->wcap : 0;
   if (tau_on && preflags == nullptr) {
     const int gx = (cols + CF_COLS - 1) / CF_COLS;
     const int64_t rps = (rows + slabs - 1) / slabs;
     hipLaunchKernelGGL(k_colflags<DT>, dim3(gx, (unsigned)slabs), dim3(256), 0, st, X, rows, cols, tau, rps, vec,
                        nwords, scratch, nullptr);
   }
-  const uint32_t* bits = preflags != nullptr ? preflags : scratch;
   // the row kernel also writes the outlier list and count (count 0 when the split is off)
   // workgroups: four rows at a time (one per wave), or one row at a time
   const int64_t rblocks = rows > 0 ? ((rows + 3) / 4 < RQ_MAX_BLOCKS ? (rows + 3) / 4 : RQ_MAX_BLOCKS) : 1;
   const int64_t wblocks = rows > 0 ? (rows < RQ_MAX_BLOCKS ? rows : RQ_MAX_BLOCKS) : 1;
   // with the weight slice to write, at least one wave per 16 weight rows (up
   // to the cap); the extra workgroups have no rows of X
-  const bool wf = ow != nullptr && ow->wsub != nullptr && ow->wcap > 0 && ow->N > 0 && tau_on;
   const int64_t fblocks = wf ? ((int64_t)ow->N + 15) / 16 : 1;
-  const int8_t* wCB = wf ? ow->CB : nullptr;
-  const float* wSCB = wf ? ow->SCB : nullptr;
-  uint16_t* wsub = wf ? ow->wsub : nullptr;
-  const int wN = wf ? ow->N : 0, wcap = wf ? ow->wcap : 0;
   const int nchunk = (cols + 7) / 8;
   const size_t lds = tau_on ? (size_t)2 * (nwords > 0 ? nwords : 1) * 4 : 0;
 #define I8L_RQ(NCH, VEC, WGM)                                                                                   \

@@ -420,19 +420,24 @@ def test_mlp600_residual_example(I8):
         cb, s = oracle.quantize_weight(W)
         layers.append((cb, s, b))
     r = oracle.mlp_forward_backward(x, g, "f32", layers, wl.threshold)
-    # GPU: int8 linears from the library; SiLU and the residual add as torch glue
+    # GPU: the int8 linears and the SiLU between them from the library (the
+    # SiLU kernel also hands the second linear its input's outlier flags);
+    # the residual add and SiLU's derivative as torch glue
     gw = [_gpu_weights(I8, W) for W in Ws]
     xt, gt = dev(x), dev(g)
     h = I8.int8_linear_forward(xt, gw[0][0], gw[0][1], dev(bs[0]), wl.threshold)
-    a = torch.nn.functional.silu(h)
-    o = I8.int8_linear_forward(a, gw[1][0], gw[1][1], dev(bs[1]), wl.threshold) + xt
+    a, flags = I8.silu_outlier_flags(h, wl.threshold)
+    o = I8.int8_linear_forward_flagged(a, flags, gw[1][0], gw[1][1], dev(bs[1])) + xt
     ga, gb2 = I8.int8_linear_backward_input(gt, gw[1][0], gw[1][1])
     sg = torch.sigmoid(h)
     gh = ga * sg * (1 + h * (1 - sg))
     gx, gb1 = I8.int8_linear_backward_input(gh, gw[0][0], gw[0][1])
     gx = gx + gt
     torch.cuda.synchronize()
+    assert_float_gate(host(a), "f32", oracle.to_f64(r["a"], "f32"), "mlp SiLU", tight_rel=2.0 ** -8)
     assert_float_gate(host(o), "f32", oracle.to_f64(r["out"], "f32"), "mlp out", tight_rel=2.0 ** -8)
     assert_float_gate(host(gx), "f32", oracle.to_f64(r["grad_x"], "f32"), "mlp grad_x", tight_rel=2.0 ** -8)
+    assert_float_gate(host(gb2), "f32", oracle.grad_bias(g, "f32")[0], "mlp grad_bias 2", tight_rel=2.0 ** -16)
+    assert_float_gate(host(gb1), "f32", oracle.grad_bias(r["g_h"], "f32")[0], "mlp grad_bias 1", tight_rel=2.0 ** -8)
     # the second layer's quantizer on the oracle's own SiLU output is bit-exact
     _check_quant(I8, r["a"], "f32", wl.threshold)

@@ -37,6 +37,12 @@
  *     errors are reported as I8L_EHIP. Faults inside kernels surface, as in
  *     HIP, at the caller's next synchronisation.
  *   - Calls are stateless and reentrant; results are bitwise deterministic.
+ *   - Graph capture: every call except int8_linear_forward_check enqueues
+ *     kernels only (no allocation, memset or synchronisation), so it can be
+ *     recorded by HIP stream capture and replayed; the pointers are captured,
+ *     so a replay reads whatever the buffers hold then. The first call of a
+ *     kernel family on a device raises that kernel's LDS limit
+ *     (hipFuncSetAttribute); make one ordinary call before capturing.
  *   - Outlier threshold tau: a feature column is an outlier column when any
  *     row of the (flattened) input has |fp16(x)| > tau (strict, compared in
  *     fp32). tau <= 0, tau = +inf or NaN disables the split.

@@ -458,8 +458,9 @@ def run_peaks():
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the first ~10 steps after an idle GPU run up to 1 % slower than the steady state
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="llama7b_block")
     ap.add_argument("--sets", type=int, default=2, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")

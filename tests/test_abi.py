@@ -342,3 +342,11 @@ def test_noalloc_forward_host_errors(L):
     assert call(M=8192, K=8192) == L.I8L_ESCRATCH     # 64 MiB of codes alone
     assert call(M=0) == L.I8L_OK and call(N=0) == L.I8L_OK
     assert b"static scratch" in L.lib.int8_linear_strerror(L.I8L_ESCRATCH)
+
+
+def test_header_compiles_as_c99_and_links(L, tmp_path):
+    """include/int8lin.h is plain C: the C caller (tests/c_abi_main.c) compiles
+    with gcc -std=c99 -Wall -Wextra -Werror and links against the library."""
+    from tests import c_abi_build
+    out = str(tmp_path / "c_abi_main")
+    assert c_abi_build.build(out) == out and os.path.exists(out)

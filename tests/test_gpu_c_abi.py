@@ -14,7 +14,9 @@ BIN = os.path.join(ROOT, "tests", "c_abi_main")
 
 @pytest.mark.gpu
 def test_plain_c_caller_integer_cases():
-    assert os.path.exists(BIN), "tests/c_abi_main is missing: run __graft_entry__.build() first"
+    if not os.path.exists(BIN):          # normally built beforehand by build()
+        from tests import c_abi_build
+        c_abi_build.build()
     print("\n  running tests/c_abi_main", flush=True)
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=180)
     print(r.stdout, r.stderr, flush=True)

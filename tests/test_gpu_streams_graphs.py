@@ -119,3 +119,86 @@ def test_graph_capture_and_replay(M, K, N):
             assert_bits_equal(host(out_na), host(ref[0]), f"replay {rep} allocation-free out")
         if rep == 0:
             _check_oracle(c, CB, SCB, *ref, f"replay {rep}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_graph_capture_other_entry_points(M, K, N):
+    """The quantizer, the SiLU producer with its flags, the flagged forward, the
+    int8 backward variant and the weight gradient, captured in one graph:
+    every replay bit-identical to the same calls made eagerly."""
+    import int8_quantized_linear_rowwise_amd as I8
+    print(f"\n  [{M}x{K}x{N} {DT}] quantizer, SiLU flags, flagged forward, int8 backward, grad_W in one graph",
+          flush=True)
+    c0, CB, SCB = _weights(I8, M, K, N, 51)
+    W = dev(c0["W"])
+    CBt, SCBt = I8.quantize_weight_colwise(W)
+    cap = I8.default_cap(K)
+    bias = dev(c0["bias"], DT)
+    sX, sH, sG = dev(c0["A"], DT), dev(c0["A"], DT), dev(c0["G"], DT)
+    bf = torch.bfloat16
+
+    def buffers():
+        return dict(codes=torch.empty((M, K), dtype=torch.int8, device="cuda:0"),
+                    scale=torch.empty((M,), dtype=torch.float32, device="cuda:0"),
+                    idx=torch.empty((cap,), dtype=torch.int32, device="cuda:0"),
+                    cnt=torch.empty((1,), dtype=torch.int32, device="cuda:0"),
+                    sub=torch.empty((M, cap), dtype=torch.float16, device="cuda:0"),
+                    qws=torch.empty((max(1, I8.lib.int8_quantize_rowwise_workspace_bytes(M, K)),),
+                                    dtype=torch.uint8, device="cuda:0"),
+                    act=torch.empty((M, K), dtype=bf, device="cuda:0"),
+                    flags=I8.outlier_flags_buffer(M, K, "cuda:0"),
+                    out=torch.empty((M, N), dtype=bf, device="cuda:0"),
+                    c32=torch.empty((M, N), dtype=torch.int32, device="cuda:0"),
+                    wsf=I8.forward_workspace(M, K, N, cap, "cuda:0"),
+                    gA8=torch.empty((M, K), dtype=bf, device="cuda:0"),
+                    gb8=torch.empty((N,), dtype=bf, device="cuda:0"),
+                    ws8=I8.backward_int8_workspace(M, N, True, "cuda:0"),
+                    gW=torch.empty((N, K), dtype=bf, device="cuda:0"))
+
+    def calls(X, H, G, b):
+        I8.check(I8.lib.int8_quantize_rowwise(X.data_ptr(), I8.DTYPE_CODE[X.dtype], M, K, 6.0, b["codes"].data_ptr(),
+                                              b["scale"].data_ptr(), b["idx"].data_ptr(), b["cnt"].data_ptr(),
+                                              b["sub"].data_ptr(), cap, b["qws"].data_ptr(), b["qws"].numel(),
+                                              torch.cuda.current_stream().cuda_stream), "int8_quantize_rowwise")
+        I8.silu_outlier_flags(H, 6.0, A=b["act"], flags=b["flags"])
+        I8.int8_linear_forward_flagged(b["act"], b["flags"], CB, SCB, bias, cap, out=b["out"], c32=b["c32"],
+                                       workspace=b["wsf"])
+        I8.int8_linear_backward_input_int8(G, CBt, SCBt, True, grad_A=b["gA8"], grad_bias=b["gb8"],
+                                           workspace=b["ws8"])
+        I8.int8_linear_backward_weight(G, X, grad_W=b["gW"])
+
+    gbuf = buffers()
+    calls(sX, sH, sG, gbuf)                 # eager warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(sX, sH, sG, gbuf)
+    torch.cuda.synchronize()
+
+    names = ("codes", "scale", "idx", "cnt", "sub", "act", "flags", "out", "c32", "gA8", "gb8", "gW")
+    for rep, seed in enumerate((52, 53)):
+        c = workloads.small_case(DT, M, K, N, seed=seed, n_outliers=4 + 3 * rep)
+        h = workloads.small_case(DT, M, K, N, seed=seed + 100, n_outliers=0)
+        sX.copy_(dev(c["A"], DT))
+        sH.copy_(dev(h["A"], DT))
+        sG.copy_(dev(c["G"], DT))
+        torch.cuda.synchronize()
+        print(f"  replay {rep} (seed {seed})", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        ebuf = buffers()
+        calls(dev(c["A"], DT), dev(h["A"], DT), dev(c["G"], DT), ebuf)
+        torch.cuda.synchronize()
+        n = int(host(gbuf["cnt"])[0])
+        assert n == int(host(ebuf["cnt"])[0])
+        for name in names:
+            a, b = host(gbuf[name]), host(ebuf[name])
+            if name == "idx":
+                a, b = a[:min(n, cap)], b[:min(n, cap)]
+            elif name == "sub":
+                a, b = a[:, :min(n, cap)], b[:, :min(n, cap)]
+            elif name == "flags":
+                w = I8.lib.int8_outlier_flags_words(M, K)
+                a, b = a[:w], b[:w]
+            assert_bits_equal(a, b, f"replay {rep} {name}")
